@@ -1,0 +1,10 @@
+"""The CPU oracle against its pins (library special cases, closed forms, invariants, page examples)."""
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=[p.__name__ for p in ALL_PINS])
+def test_oracle_pin(pin):
+    pin(oracle.load())
