@@ -1,0 +1,213 @@
+/*
+ * sattn.h -- C ABI of libsattn: index-gathered attention forward with online
+ * softmax for AMD Instinct MI355X (gfx950).
+ *
+ * For every query token there is a set of keys.  The library computes
+ *     o = softmax(scale * q . k^T + sink term) . v
+ * over that set only, and optionally the natural-log log-sum-exp of the
+ * logits.  The key set is either
+ *   - a sliding window inside one sequence of a varlen batch (vLLM PR #49815
+ *     report, "关键源码片段": `context_attention_fwd` takes q, k, v, o,
+ *     per-sequence start/length from cu_seqlens, the softmax scale, a q-side
+ *     and a k-side window width and per-head sinks; its test reference builds
+ *     GQA with repeat_interleave and masks |i - j| > window), or
+ *   - an explicit top-k list of rows of a single-head cache whose row is read
+ *     as both key and value (DeepSeek-V4 CSA/HCA article, §3.3 cache layout
+ *     and §4.2 gather: `topk_idxs[b, m, k]` holds absolute cache rows, -1
+ *     marks an unused slot).
+ *
+ * Sink semantics (vLLM report, `_fwd_kernel` sink branch; DeepSeek-V4 article
+ * §4.4):
+ *   SATTN_SINK_KEY0_BIAS  sinks[h] is added to the logit of key 0 (the first
+ *                         token of the sequence on the window path, cache row 0
+ *                         on the indexed path) when that key is in the set;
+ *   SATTN_SINK_NULL_LOGIT sinks[h] is a logit with no value: exp(sinks[h])
+ *                         enters the softmax denominator only.
+ * Sinks are in natural-logit units and are not multiplied by the scale.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     allocates nothing, keeps no pointer after returning and holds no mutable
+ *     global state, so it may be called from several host threads.
+ *   - Every kernel is enqueued on `stream` (the split-K merge included);
+ *     nothing runs on the default stream unless `stream` is it, and nothing
+ *     synchronises.  A caller that produces inputs on another stream must make
+ *     `stream` wait on it (an event), as the nano-vllm offload note's stream
+ *     fix shows.
+ *   - Arguments are validated on the host before any launch; on error a status
+ *     is returned and nothing is enqueued.  A launch failure returns
+ *     SATTN_ERR_LAUNCH.  Faults inside kernels surface at the caller's next
+ *     synchronisation.
+ *   - Tensors are dense, row-major (last dimension contiguous); q/k/v/o/kv
+ *     must be 16-byte aligned and head_dim a multiple of 8.
+ *   - Output rows whose key set is empty get o = 0 and lse = -inf (with a null
+ *     sink: lse = sinks[h]).
+ */
+#ifndef SATTN_H
+#define SATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SATTN_ABI_VERSION 1
+
+typedef enum {
+  SATTN_OK = 0,
+  SATTN_ERR_NULL_PTR = 1,    /* a required pointer is NULL                        */
+  SATTN_ERR_SHAPE = 2,       /* a size is negative/zero or inconsistent           */
+  SATTN_ERR_DTYPE = 3,       /* unknown dtype                                     */
+  SATTN_ERR_UNSUPPORTED = 4, /* valid but not implemented (e.g. head_dim > 256)   */
+  SATTN_ERR_ALIGNMENT = 5,   /* a tensor pointer is not 16-byte aligned           */
+  SATTN_ERR_WORKSPACE = 6,   /* split-K workspace missing or too small            */
+  SATTN_ERR_LAUNCH = 7,      /* the HIP runtime rejected a kernel launch          */
+  SATTN_ERR_ARG = 8          /* bad enum value or option                          */
+} sattn_status;
+
+typedef enum { SATTN_BF16 = 0, SATTN_F32 = 1 } sattn_dtype;
+
+typedef enum {
+  SATTN_SINK_NONE = 0,
+  SATTN_SINK_KEY0_BIAS = 1,
+  SATTN_SINK_NULL_LOGIT = 2
+} sattn_sink_mode;
+
+/*
+ * Sliding-window attention over a varlen batch.
+ *
+ *   q   [total_tokens, num_heads,    head_dim]  dtype
+ *   k,v [total_tokens, num_kv_heads, head_dim]  dtype
+ *   o   [total_tokens, num_heads,    head_dim]  dtype (written)
+ *   lse [total_tokens, num_heads] fp32, natural log (written; may be NULL)
+ *   cu_seqlens  device int32 [num_seqs + 1]: cu[0] = 0, non-decreasing,
+ *               cu[num_seqs] = total_tokens; sequence s owns tokens
+ *               [cu[s], cu[s+1]).  Zero-length sequences are allowed.
+ *   max_seqlen  an upper bound of every sequence length (sizes the grid);
+ *               tokens past max_seqlen in a longer sequence are NOT computed,
+ *               as with the page's max_input_len.
+ *   Query head h reads KV head h / (num_heads / num_kv_heads).
+ *   Query i of a sequence attends key j of the same sequence iff
+ *       (window_left  < 0 or j >= i - window_left) and
+ *       (window_right < 0 or j <= i + window_right).
+ *   A symmetric window of width w is (w, w); causal is (w - 1, 0) for a
+ *   w-token window including the query itself, or (-1, 0) for full causal.
+ *   sinks: device fp32 [num_heads]; required unless sink_mode is NONE.
+ */
+typedef struct {
+  sattn_dtype dtype;
+  const void *q;
+  const void *k;
+  const void *v;
+  void *o;
+  float *lse;
+  const int32_t *cu_seqlens;
+  int32_t num_seqs;
+  int32_t total_tokens;
+  int32_t max_seqlen;
+  int32_t num_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t window_left;
+  int32_t window_right;
+  float softmax_scale;
+  const float *sinks;
+  sattn_sink_mode sink_mode;
+} sattn_window_args;
+
+/*
+ * Top-k index-gathered attention over a single-head cache shared by all
+ * query heads (each cache row is both key and value).
+ *
+ *   q         [batch, q_len, num_heads, head_dim]  dtype
+ *   kv        [batch, kv_len, head_dim]            dtype
+ *   topk_idxs [batch, q_len, topk] int32: absolute rows of kv[b]; any value
+ *             outside [0, kv_len) (the documented one is -1) is not a key.
+ *             Valid entries of one list must be distinct (a repeated row
+ *             would be counted twice).  List order does not matter.
+ *   o         [batch, q_len, num_heads, head_dim]  dtype (written)
+ *   lse       [batch, q_len, num_heads] fp32 natural log (written; may be NULL)
+ *   num_splits 1: one pass.  S > 1: the list is cut into S contiguous slices
+ *             of ceil(topk / S) entries; each slice's normalised partial
+ *             output and log-sum-exp go to `workspace`, then a second kernel
+ *             on the same stream merges them (sattn_merge_lse) into o / lse.
+ *             A null sink enters once, in the merge; a key-0 bias applies in
+ *             the slice that holds row 0.  1 <= S <= topk is required.
+ *   workspace  device buffer of at least
+ *             sattn_indexed_workspace_size(batch, q_len, num_heads, head_dim, S)
+ *             bytes, 256-byte aligned (may be NULL when S == 1).
+ */
+typedef struct {
+  sattn_dtype dtype;
+  const void *q;
+  const void *kv;
+  const int32_t *topk_idxs;
+  void *o;
+  float *lse;
+  int32_t batch;
+  int32_t q_len;
+  int32_t num_heads;
+  int32_t head_dim;
+  int32_t kv_len;
+  int32_t topk;
+  float softmax_scale;
+  const float *sinks;
+  sattn_sink_mode sink_mode;
+  int32_t num_splits;
+  void *workspace;
+  size_t workspace_bytes;
+} sattn_indexed_args;
+
+/*
+ * Merge of per-chunk partial results (the nano-vllm offload note's
+ * three-stage KV chunking: partial softmax statistics per chunk, merged into
+ * global ones).
+ *
+ *   part_o   [num_parts, rows, num_heads, head_dim] fp32: each part's output
+ *            normalised by its own denominator
+ *   part_lse [num_parts, rows, num_heads] fp32: each part's log-sum-exp;
+ *            -inf marks a part with no key (its part_o is ignored)
+ *   sink_mode NONE or NULL_LOGIT (the null sink is added to the merged
+ *            denominator once); KEY0_BIAS is rejected (it belongs to a part).
+ *   o        [rows, num_heads, head_dim] out_dtype (written)
+ *   lse      [rows, num_heads] fp32 natural log (written; may be NULL)
+ *   o_m = sum_c exp(lse_c - M) o_c / W,  W = sum_c exp(lse_c - M) [+ exp(sink - M)],
+ *   lse = M + log W,  M = max(lse_c, sink).
+ */
+typedef struct {
+  const float *part_o;
+  const float *part_lse;
+  int32_t num_parts;
+  int32_t rows;
+  int32_t num_heads;
+  int32_t head_dim;
+  const float *sinks;
+  sattn_sink_mode sink_mode;
+  sattn_dtype out_dtype;
+  void *o;
+  float *lse;
+} sattn_merge_args;
+
+sattn_status sattn_window_fwd(const sattn_window_args *args, hipStream_t stream);
+sattn_status sattn_indexed_fwd(const sattn_indexed_args *args, hipStream_t stream);
+sattn_status sattn_merge_lse(const sattn_merge_args *args, hipStream_t stream);
+
+/* Bytes of split-K workspace sattn_indexed_fwd needs (0 when num_splits <= 1). */
+size_t sattn_indexed_workspace_size(int32_t batch, int32_t q_len, int32_t num_heads,
+                                    int32_t head_dim, int32_t num_splits);
+
+/* Static, NUL-terminated description of a status code. */
+const char *sattn_status_string(sattn_status status);
+
+/* SATTN_ABI_VERSION of the loaded library. */
+int sattn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SATTN_H */

@@ -1,0 +1,225 @@
+"""Python binding of libsattn (index-gathered attention forward on MI355X).
+
+Argument marshalling only: tensors supply device pointers and sizes, the
+stream is torch's current stream, and every step of the computation runs in
+the HIP kernels of libsattn.so.  There is no fallback: if the library is not
+built, importing works but every call raises.
+
+    o = window_fwd(q, k, v, cu_seqlens, max_seqlen, window=(128, 128),
+                   sinks=sinks, sink_mode="key0")
+    o = indexed_fwd(q, kv, topk_idxs, sinks=sinks, sink_mode="null", num_splits=8)
+    o = merge_lse(part_o, part_lse, sinks=sinks, sink_mode="null")
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch  # loads the HIP runtime libsattn links against
+
+__all__ = ["window_fwd", "indexed_fwd", "merge_lse", "indexed_workspace_size", "SattnError", "library_path",
+           "load_library", "abi_version", "SINK_MODES"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_NAME = "libsattn.so"
+SINK_MODES = {"none": 0, "key0": 1, "null": 2}
+_DTYPES = {torch.bfloat16: 0, torch.float32: 1}
+
+
+class SattnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = _lib_handle().sattn_status_string(status).decode() if _LIB is not None else str(status)
+        super().__init__(f"{where}: {msg} (status {status})")
+        self.status = status
+
+
+class _WindowArgs(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int), ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("o", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("cu_seqlens", ctypes.c_void_p),
+                ("num_seqs", ctypes.c_int32), ("total_tokens", ctypes.c_int32), ("max_seqlen", ctypes.c_int32),
+                ("num_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("window_left", ctypes.c_int32), ("window_right", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float), ("sinks", ctypes.c_void_p), ("sink_mode", ctypes.c_int)]
+
+
+class _IndexedArgs(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int), ("q", ctypes.c_void_p), ("kv", ctypes.c_void_p),
+                ("topk_idxs", ctypes.c_void_p), ("o", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+                ("batch", ctypes.c_int32), ("q_len", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("kv_len", ctypes.c_int32), ("topk", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float), ("sinks", ctypes.c_void_p), ("sink_mode", ctypes.c_int),
+                ("num_splits", ctypes.c_int32), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class _MergeArgs(ctypes.Structure):
+    _fields_ = [("part_o", ctypes.c_void_p), ("part_lse", ctypes.c_void_p), ("num_parts", ctypes.c_int32),
+                ("rows", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("sinks", ctypes.c_void_p), ("sink_mode", ctypes.c_int), ("out_dtype", ctypes.c_int),
+                ("o", ctypes.c_void_p), ("lse", ctypes.c_void_p)]
+
+
+_LIB = None
+
+
+def library_path() -> str:
+    return os.environ.get("SATTN_LIBRARY", os.path.join(_PKG, LIB_NAME))
+
+
+def load_library(path: str | None = None):
+    """Load libsattn.so and declare its C ABI.  Raises if the library has not been built."""
+    path = path or library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m sliding_window_attention_index_amd.build`")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    lib.sattn_window_fwd.argtypes = [ctypes.POINTER(_WindowArgs), P]
+    lib.sattn_window_fwd.restype = ctypes.c_int
+    lib.sattn_indexed_fwd.argtypes = [ctypes.POINTER(_IndexedArgs), P]
+    lib.sattn_indexed_fwd.restype = ctypes.c_int
+    lib.sattn_merge_lse.argtypes = [ctypes.POINTER(_MergeArgs), P]
+    lib.sattn_merge_lse.restype = ctypes.c_int
+    lib.sattn_indexed_workspace_size.argtypes = [ctypes.c_int32] * 5
+    lib.sattn_indexed_workspace_size.restype = ctypes.c_size_t
+    lib.sattn_status_string.argtypes = [ctypes.c_int]
+    lib.sattn_status_string.restype = ctypes.c_char_p
+    lib.sattn_abi_version.argtypes = []
+    lib.sattn_abi_version.restype = ctypes.c_int
+    return lib
+
+
+def _lib_handle():
+    global _LIB
+    if _LIB is None:
+        _LIB = load_library()
+    return _LIB
+
+
+def abi_version() -> int:
+    return _lib_handle().sattn_abi_version()
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(dev) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _check_dev(name, t, dev, dtype=None):
+    if not t.is_cuda or t.device != dev:
+        raise ValueError(f"{name} must be on {dev}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _sink_mode(mode, sinks):
+    m = SINK_MODES[mode] if isinstance(mode, str) else int(mode)
+    if m != 0 and sinks is None:
+        raise ValueError("sinks are required for this sink_mode")
+    return m
+
+
+def window_fwd(q, k, v, cu_seqlens, max_seqlen: int, *, window=(-1, -1), softmax_scale: float | None = None,
+               sinks=None, sink_mode="none", out=None, return_lse: bool = False):
+    """Sliding-window attention over a varlen batch (see include/sattn.h, sattn_window_args).
+
+    q [T,H,D], k/v [T,Hkv,D] (bf16 or fp32), cu_seqlens int32 [S+1] on the same device.
+    window=(left, right): key j attends query i iff i-left <= j <= i+right (negative = unbounded).
+    """
+    dev = q.device
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(name, t, dev, dt)
+    _check_dev("cu_seqlens", cu_seqlens, dev, torch.int32)
+    T, H, D = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (T, Hkv, D) or v.shape != (T, Hkv, D):
+        raise ValueError("k and v must be [T, Hkv, D] like q")
+    mode = _sink_mode(sink_mode, sinks)
+    if sinks is not None:
+        _check_dev("sinks", sinks, dev, torch.float32)
+    o = torch.empty_like(q) if out is None else out
+    _check_dev("out", o, dev, dt)
+    lse = torch.empty((T, H), dtype=torch.float32, device=dev) if return_lse else None
+    a = _WindowArgs(_DTYPES[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens),
+                    cu_seqlens.numel() - 1, T, int(max_seqlen), H, Hkv, D, int(window[0]), int(window[1]),
+                    float(1.0 / math.sqrt(D) if softmax_scale is None else softmax_scale),
+                    _ptr(sinks) if mode else None, mode)
+    st = _lib_handle().sattn_window_fwd(ctypes.byref(a), _stream(dev))
+    if st != 0:
+        raise SattnError(st, "sattn_window_fwd")
+    return (o, lse) if return_lse else o
+
+
+def indexed_workspace_size(batch: int, q_len: int, num_heads: int, head_dim: int, num_splits: int) -> int:
+    return int(_lib_handle().sattn_indexed_workspace_size(batch, q_len, num_heads, head_dim, num_splits))
+
+
+def indexed_fwd(q, kv, topk_idxs, *, softmax_scale: float | None = None, sinks=None, sink_mode="none",
+                num_splits: int = 1, out=None, return_lse: bool = False, workspace=None):
+    """Top-k gathered attention over a shared K=V cache (see include/sattn.h, sattn_indexed_args).
+
+    q [B,M,H,D], kv [B,N,D] (bf16 or fp32), topk_idxs int32 [B,M,K] (-1 = unused).
+    num_splits > 1 cuts each list into slices merged by a second kernel; the
+    workspace (uint8, 256-byte aligned) is allocated here unless given.
+    """
+    dev = q.device
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    _check_dev("q", q, dev, dt)
+    _check_dev("kv", kv, dev, dt)
+    _check_dev("topk_idxs", topk_idxs, dev, torch.int32)
+    B, M, H, D = q.shape
+    N = kv.shape[1]
+    K = topk_idxs.shape[2]
+    if kv.shape != (B, N, D) or topk_idxs.shape[:2] != (B, M):
+        raise ValueError("kv must be [B, N, D] and topk_idxs [B, M, K]")
+    mode = _sink_mode(sink_mode, sinks)
+    if sinks is not None:
+        _check_dev("sinks", sinks, dev, torch.float32)
+    o = torch.empty_like(q) if out is None else out
+    _check_dev("out", o, dev, dt)
+    lse = torch.empty((B, M, H), dtype=torch.float32, device=dev) if return_lse else None
+    ws_bytes = indexed_workspace_size(B, M, H, D, num_splits)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _check_dev("workspace", workspace, dev)
+    a = _IndexedArgs(_DTYPES[dt], _ptr(q), _ptr(kv), _ptr(topk_idxs), _ptr(o), _ptr(lse), B, M, H, D, N, K,
+                     float(1.0 / math.sqrt(D) if softmax_scale is None else softmax_scale),
+                     _ptr(sinks) if mode else None, mode, int(num_splits), _ptr(workspace),
+                     0 if workspace is None else workspace.numel() * workspace.element_size())
+    st = _lib_handle().sattn_indexed_fwd(ctypes.byref(a), _stream(dev))
+    if st != 0:
+        raise SattnError(st, "sattn_indexed_fwd")
+    return (o, lse) if return_lse else o
+
+
+def merge_lse(part_o, part_lse, *, sinks=None, sink_mode="none", out_dtype=torch.bfloat16, out=None,
+              return_lse: bool = False):
+    """Merge partial (o_c, lse_c) results: part_o fp32 [S,R,H,D], part_lse fp32 [S,R,H]."""
+    dev = part_o.device
+    _check_dev("part_o", part_o, dev, torch.float32)
+    _check_dev("part_lse", part_lse, dev, torch.float32)
+    S, R, H, D = part_o.shape
+    if part_lse.shape != (S, R, H):
+        raise ValueError("part_lse must be [S, R, H]")
+    mode = _sink_mode(sink_mode, sinks)
+    if sinks is not None:
+        _check_dev("sinks", sinks, dev, torch.float32)
+    o = torch.empty((R, H, D), dtype=out_dtype, device=dev) if out is None else out
+    _check_dev("out", o, dev, out_dtype)
+    lse = torch.empty((R, H), dtype=torch.float32, device=dev) if return_lse else None
+    a = _MergeArgs(_ptr(part_o), _ptr(part_lse), S, R, H, D, _ptr(sinks) if mode else None, mode,
+                   _DTYPES[out_dtype], _ptr(o), _ptr(lse))
+    st = _lib_handle().sattn_merge_lse(ctypes.byref(a), _stream(dev))
+    if st != 0:
+        raise SattnError(st, "sattn_merge_lse")
+    return (o, lse) if return_lse else o

@@ -1,0 +1,214 @@
+// C ABI of libsattn: host-side validation and kernel dispatch.
+//
+// Every argument is checked here before anything is enqueued; an invalid call
+// returns a status and touches neither the device nor the stream.  All
+// launches go to the caller's stream and nothing synchronises (the nano-vllm
+// offload note's lesson: kernels that run on a stream other than the one the
+// producer's event was waited on read unfinished data).
+#include "sattn.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "sattn_kernels.hpp"
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool valid_dtype(sattn_dtype t) { return t == SATTN_BF16 || t == SATTN_F32; }
+bool valid_sink(sattn_sink_mode m) {
+  return m == SATTN_SINK_NONE || m == SATTN_SINK_KEY0_BIAS || m == SATTN_SINK_NULL_LOGIT;
+}
+
+sattn_status head_dim_status(int32_t d) {
+  if (d <= 0) return SATTN_ERR_SHAPE;
+  if (d % 8 != 0 || d > 256) return SATTN_ERR_UNSUPPORTED;
+  return SATTN_OK;
+}
+
+sattn_status launch_status(hipError_t e) { return e == hipSuccess ? SATTN_OK : SATTN_ERR_LAUNCH; }
+
+// Split-K workspace layout: part_o [S, R, H, D] fp32, then part_lse [S, R, H] fp32,
+// each starting on a 256-byte boundary.
+size_t part_o_bytes(int64_t parts, int64_t rows, int64_t heads, int64_t dim) {
+  return round_up(static_cast<size_t>(parts * rows * heads * dim) * sizeof(float), 256);
+}
+size_t part_lse_bytes(int64_t parts, int64_t rows, int64_t heads) {
+  return round_up(static_cast<size_t>(parts * rows * heads) * sizeof(float), 256);
+}
+
+}  // namespace
+
+extern "C" {
+
+int sattn_abi_version(void) { return SATTN_ABI_VERSION; }
+
+const char *sattn_status_string(sattn_status s) {
+  switch (s) {
+    case SATTN_OK: return "ok";
+    case SATTN_ERR_NULL_PTR: return "a required pointer is NULL";
+    case SATTN_ERR_SHAPE: return "invalid or inconsistent sizes";
+    case SATTN_ERR_DTYPE: return "unknown dtype";
+    case SATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case SATTN_ERR_ALIGNMENT: return "tensor pointer not 16-byte aligned";
+    case SATTN_ERR_WORKSPACE: return "split-K workspace missing, misaligned or too small";
+    case SATTN_ERR_LAUNCH: return "kernel launch failed";
+    case SATTN_ERR_ARG: return "invalid enum value or option";
+  }
+  return "unknown status";
+}
+
+size_t sattn_indexed_workspace_size(int32_t batch, int32_t q_len, int32_t num_heads, int32_t head_dim,
+                                    int32_t num_splits) {
+  if (num_splits <= 1 || batch <= 0 || q_len <= 0 || num_heads <= 0 || head_dim <= 0) return 0;
+  const int64_t rows = static_cast<int64_t>(batch) * q_len;
+  return part_o_bytes(num_splits, rows, num_heads, head_dim) + part_lse_bytes(num_splits, rows, num_heads);
+}
+
+sattn_status sattn_window_fwd(const sattn_window_args *a, hipStream_t stream) {
+  if (!a) return SATTN_ERR_NULL_PTR;
+  if (!valid_dtype(a->dtype)) return SATTN_ERR_DTYPE;
+  if (!valid_sink(a->sink_mode)) return SATTN_ERR_ARG;
+  if (a->num_seqs < 0 || a->total_tokens < 0 || a->max_seqlen < 0 || a->num_heads <= 0 ||
+      a->num_kv_heads <= 0 || a->num_heads % a->num_kv_heads != 0)
+    return SATTN_ERR_SHAPE;
+  if (sattn_status s = head_dim_status(a->head_dim)) return s;
+  if (!isfinite(a->softmax_scale)) return SATTN_ERR_ARG;
+  if (a->total_tokens == 0 || a->num_seqs == 0) return SATTN_OK;
+  if (a->max_seqlen == 0) return SATTN_ERR_SHAPE;
+  if (!a->q || !a->k || !a->v || !a->o || !a->cu_seqlens) return SATTN_ERR_NULL_PTR;
+  if (a->sink_mode != SATTN_SINK_NONE && !a->sinks) return SATTN_ERR_NULL_PTR;
+  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o) ||
+      !aligned4(a->cu_seqlens) || (a->lse && !aligned4(a->lse)) || (a->sinks && !aligned4(a->sinks)))
+    return SATTN_ERR_ALIGNMENT;
+
+  sattn::WindowParams p;
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.o = a->o;
+  p.lse = a->lse;
+  p.cu_seqlens = a->cu_seqlens;
+  p.num_seqs = a->num_seqs;
+  p.max_seqlen = a->max_seqlen;
+  p.num_heads = a->num_heads;
+  p.num_kv_heads = a->num_kv_heads;
+  p.head_dim = a->head_dim;
+  p.group = a->num_heads / a->num_kv_heads;
+  p.window_left = a->window_left;
+  p.window_right = a->window_right;
+  p.scale_log2 = a->softmax_scale * 1.4426950408889634f;
+  p.sinks = a->sink_mode != SATTN_SINK_NONE ? a->sinks : nullptr;
+  p.sink_mode = a->sink_mode;
+  if (a->dtype == SATTN_BF16 && sattn::window_mfma_supported(p))
+    return launch_status(sattn::launch_window_mfma(p, stream));
+  return launch_status(sattn::launch_window_valu(p, a->dtype == SATTN_F32 ? sattn::kF32 : sattn::kBF16, stream));
+}
+
+sattn_status sattn_merge_lse(const sattn_merge_args *a, hipStream_t stream) {
+  if (!a) return SATTN_ERR_NULL_PTR;
+  if (!valid_dtype(a->out_dtype)) return SATTN_ERR_DTYPE;
+  if (a->sink_mode != SATTN_SINK_NONE && a->sink_mode != SATTN_SINK_NULL_LOGIT) return SATTN_ERR_ARG;
+  if (a->num_parts < 0 || a->rows < 0 || a->num_heads <= 0) return SATTN_ERR_SHAPE;
+  if (sattn_status s = head_dim_status(a->head_dim)) return s;
+  if (a->rows == 0) return SATTN_OK;
+  if (!a->o || (a->num_parts > 0 && (!a->part_o || !a->part_lse))) return SATTN_ERR_NULL_PTR;
+  if (a->sink_mode == SATTN_SINK_NULL_LOGIT && !a->sinks) return SATTN_ERR_NULL_PTR;
+  if (!aligned16(a->o) || (a->part_o && !aligned4(a->part_o)) || (a->part_lse && !aligned4(a->part_lse)) ||
+      (a->lse && !aligned4(a->lse)))
+    return SATTN_ERR_ALIGNMENT;
+  sattn::MergeParams p;
+  p.part_o = a->part_o;
+  p.part_lse = a->part_lse;
+  p.num_parts = a->num_parts;
+  p.rows = a->rows;
+  p.num_heads = a->num_heads;
+  p.head_dim = a->head_dim;
+  p.sinks = a->sinks;
+  p.sink_mode = a->sink_mode;
+  p.out_type = a->out_dtype == SATTN_F32 ? sattn::kF32 : sattn::kBF16;
+  p.o = a->o;
+  p.lse = a->lse;
+  return launch_status(sattn::launch_merge(p, stream));
+}
+
+sattn_status sattn_indexed_fwd(const sattn_indexed_args *a, hipStream_t stream) {
+  if (!a) return SATTN_ERR_NULL_PTR;
+  if (!valid_dtype(a->dtype)) return SATTN_ERR_DTYPE;
+  if (!valid_sink(a->sink_mode)) return SATTN_ERR_ARG;
+  if (a->batch < 0 || a->q_len < 0 || a->num_heads <= 0 || a->kv_len < 0 || a->topk < 0)
+    return SATTN_ERR_SHAPE;
+  if (sattn_status s = head_dim_status(a->head_dim)) return s;
+  if (!isfinite(a->softmax_scale)) return SATTN_ERR_ARG;
+  if (a->num_splits < 1 || a->num_splits > (a->topk > 0 ? a->topk : 1)) return SATTN_ERR_ARG;
+  const int64_t rows = static_cast<int64_t>(a->batch) * a->q_len;
+  if (rows == 0) return SATTN_OK;
+  if (rows > INT32_MAX) return SATTN_ERR_UNSUPPORTED;
+  if (!a->q || !a->o || (a->topk > 0 && !a->topk_idxs) || (a->kv_len > 0 && !a->kv)) return SATTN_ERR_NULL_PTR;
+  if (a->sink_mode != SATTN_SINK_NONE && !a->sinks) return SATTN_ERR_NULL_PTR;
+  if (!aligned16(a->q) || !aligned16(a->o) || (a->kv && !aligned16(a->kv)) ||
+      (a->topk_idxs && !aligned4(a->topk_idxs)) || (a->lse && !aligned4(a->lse)) ||
+      (a->sinks && !aligned4(a->sinks)))
+    return SATTN_ERR_ALIGNMENT;
+
+  sattn::IndexedParams p;
+  p.q = a->q;
+  p.kv = a->kv;
+  p.idx = a->topk_idxs;
+  p.o = a->o;
+  p.lse = a->lse;
+  p.batch = a->batch;
+  p.q_len = a->q_len;
+  p.num_heads = a->num_heads;
+  p.head_dim = a->head_dim;
+  p.kv_len = a->kv_len;
+  p.topk = a->topk;
+  p.scale_log2 = a->softmax_scale * 1.4426950408889634f;
+  p.sinks = a->sink_mode != SATTN_SINK_NONE ? a->sinks : nullptr;
+  p.sink_mode = a->sink_mode;
+  p.num_parts = 1;
+  p.part_len = a->topk;
+  p.part_o = nullptr;
+  p.part_lse = nullptr;
+
+  int parts = 1;
+  if (a->num_splits > 1) {
+    const size_t need = sattn_indexed_workspace_size(a->batch, a->q_len, a->num_heads, a->head_dim, a->num_splits);
+    if (!a->workspace || (reinterpret_cast<uintptr_t>(a->workspace) & 255u) || a->workspace_bytes < need)
+      return SATTN_ERR_WORKSPACE;
+    p.part_len = (a->topk + a->num_splits - 1) / a->num_splits;
+    parts = (a->topk + p.part_len - 1) / p.part_len;  // slices that hold at least one entry
+  }
+  const int elem = a->dtype == SATTN_F32 ? sattn::kF32 : sattn::kBF16;
+  const bool mfma = a->dtype == SATTN_BF16;
+  if (parts == 1) {
+    p.part_len = a->topk > 0 ? a->topk : 1;
+    if (mfma && sattn::indexed_mfma_supported(p)) return launch_status(sattn::launch_indexed_mfma(p, stream));
+    return launch_status(sattn::launch_indexed_valu(p, elem, stream));
+  }
+  char *ws = static_cast<char *>(a->workspace);
+  p.num_parts = parts;
+  p.part_o = reinterpret_cast<float *>(ws);
+  p.part_lse = reinterpret_cast<float *>(ws + part_o_bytes(a->num_splits, rows, a->num_heads, a->head_dim));
+  hipError_t e = (mfma && sattn::indexed_mfma_supported(p)) ? sattn::launch_indexed_mfma(p, stream)
+                                                             : sattn::launch_indexed_valu(p, elem, stream);
+  if (e != hipSuccess) return SATTN_ERR_LAUNCH;
+  sattn::MergeParams m;
+  m.part_o = p.part_o;
+  m.part_lse = p.part_lse;
+  m.num_parts = parts;
+  m.rows = static_cast<int>(rows);
+  m.num_heads = a->num_heads;
+  m.head_dim = a->head_dim;
+  m.sinks = p.sinks;
+  m.sink_mode = a->sink_mode == SATTN_SINK_NULL_LOGIT ? SATTN_SINK_NULL_LOGIT : SATTN_SINK_NONE;
+  m.out_type = elem;
+  m.o = a->o;
+  m.lse = a->lse;
+  return launch_status(sattn::launch_merge(m, stream));
+}
+
+}  // extern "C"

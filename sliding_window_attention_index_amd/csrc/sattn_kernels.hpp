@@ -1,0 +1,65 @@
+// Internal launch interface between the C ABI layer (sattn_api.cpp) and the
+// kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sattn {
+
+enum ElemType : int { kBF16 = 0, kF32 = 1 };
+
+// Window path: varlen batch, GQA, key set = band around each query.
+struct WindowParams {
+  const void *q, *k, *v;
+  void *o;
+  float *lse;                 // may be null
+  const int32_t *cu_seqlens;  // [num_seqs + 1]
+  int num_seqs, max_seqlen;
+  int num_heads, num_kv_heads, head_dim, group;  // group = num_heads / num_kv_heads
+  int window_left, window_right;                 // < 0: unbounded
+  float scale_log2;                              // softmax_scale * log2(e)
+  const float *sinks;                            // [num_heads] or null
+  int sink_mode;
+};
+
+// Indexed path: one shared K=V head per batch row, top-k lists.
+struct IndexedParams {
+  const void *q;        // [B, M, H, D]
+  const void *kv;       // [B, N, D]
+  const int32_t *idx;   // [B, M, K]
+  void *o;              // [B, M, H, D] (single pass)
+  float *lse;           // [B, M, H] or null
+  int batch, q_len, num_heads, head_dim, kv_len, topk;
+  float scale_log2;
+  const float *sinks;
+  int sink_mode;
+  int num_parts;        // slices of the list; 1 = single pass
+  int part_len;         // entries per slice (ceil(topk / num_parts))
+  float *part_o;        // [num_parts, B*M, H, D] when num_parts > 1
+  float *part_lse;      // [num_parts, B*M, H]
+};
+
+struct MergeParams {
+  const float *part_o, *part_lse;
+  int num_parts, rows, num_heads, head_dim;
+  const float *sinks;
+  int sink_mode;        // none or null
+  int out_type;         // ElemType
+  void *o;
+  float *lse;
+};
+
+// Launchers return hipSuccess or the launch error; they never synchronise.
+hipError_t launch_window_valu(const WindowParams &p, int elem_type, hipStream_t stream);
+hipError_t launch_indexed_valu(const IndexedParams &p, int elem_type, hipStream_t stream);
+hipError_t launch_merge(const MergeParams &p, hipStream_t stream);
+
+// MFMA (bf16) kernels.  `supported` tells whether a shape has an MFMA variant.
+bool window_mfma_supported(const WindowParams &p);
+hipError_t launch_window_mfma(const WindowParams &p, hipStream_t stream);
+bool indexed_mfma_supported(const IndexedParams &p);
+hipError_t launch_indexed_mfma(const IndexedParams &p, hipStream_t stream);
+
+}  // namespace sattn

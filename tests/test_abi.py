@@ -1,0 +1,152 @@
+"""C ABI checks that need no GPU: the library loads, exports what include/sattn.h declares,
+and host-side validation rejects bad arguments before anything touches the device.
+
+Every call here fails validation (or is a pure host query), so the HIP runtime
+is never asked to launch anything.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sliding_window_attention_index_amd as sattn
+from sliding_window_attention_index_amd import _IndexedArgs, _MergeArgs, _WindowArgs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sattn.h")
+
+OK, NULL_PTR, SHAPE, DTYPE, UNSUPPORTED, ALIGNMENT, WORKSPACE, LAUNCH, ARG = range(9)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    path = sattn.library_path()
+    if not os.path.exists(path):
+        from sliding_window_attention_index_amd.build import build
+        build()
+    return sattn.load_library(path)
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:sattn_status|size_t|const char \*|int)\s*(sattn_\w+)\s*\(", text, re.M)))
+
+
+def test_header_functions_exported(lib):
+    names = _declared_functions()
+    assert set(names) == {"sattn_window_fwd", "sattn_indexed_fwd", "sattn_merge_lse",
+                          "sattn_indexed_workspace_size", "sattn_status_string", "sattn_abi_version"}
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_strings(lib):
+    m = re.search(r"#define SATTN_ABI_VERSION (\d+)", open(HEADER).read())
+    assert lib.sattn_abi_version() == int(m.group(1))
+    seen = set()
+    for s in range(9):
+        txt = lib.sattn_status_string(s).decode()
+        assert txt and txt != "unknown status"
+        seen.add(txt)
+    assert len(seen) == 9
+    assert lib.sattn_status_string(99).decode() == "unknown status"
+
+
+def test_workspace_size(lib):
+    ws = lib.sattn_indexed_workspace_size
+    assert ws(64, 1, 64, 128, 1) == 0
+    # part_o [8,64,64,128] fp32 and part_lse [8,64,64] fp32, each rounded up to 256 bytes
+    assert ws(64, 1, 64, 128, 8) == 8 * 64 * 64 * 128 * 4 + 8 * 64 * 64 * 4
+    assert ws(3, 5, 7, 8, 3) == ((3 * 15 * 7 * 8 * 4 + 255) // 256 * 256) + ((3 * 15 * 7 * 4 + 255) // 256 * 256)
+    assert ws(0, 5, 7, 8, 3) == 0
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails validation first
+
+
+def _window(**kw):
+    base = dict(dtype=0, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, cu_seqlens=FAKE, num_seqs=2, total_tokens=42,
+                max_seqlen=37, num_heads=4, num_kv_heads=2, head_dim=64, window_left=8, window_right=8,
+                softmax_scale=0.125, sinks=FAKE, sink_mode=1)
+    base.update(kw)
+    return _WindowArgs(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), DTYPE),
+    (dict(sink_mode=5), ARG),
+    (dict(num_heads=4, num_kv_heads=3), SHAPE),
+    (dict(num_heads=0), SHAPE),
+    (dict(head_dim=12), UNSUPPORTED),
+    (dict(head_dim=264), UNSUPPORTED),
+    (dict(head_dim=0), SHAPE),
+    (dict(softmax_scale=float("nan")), ARG),
+    (dict(max_seqlen=0), SHAPE),
+    (dict(q=None), NULL_PTR),
+    (dict(cu_seqlens=None), NULL_PTR),
+    (dict(sinks=None), NULL_PTR),
+    (dict(o=FAKE + 8), ALIGNMENT),
+    (dict(k=FAKE + 2), ALIGNMENT),
+])
+def test_window_validation(lib, kw, status):
+    assert lib.sattn_window_fwd(ctypes.byref(_window(**kw)), None) == status
+
+
+def test_window_null_args(lib):
+    assert lib.sattn_window_fwd(None, None) == NULL_PTR
+
+
+def test_window_empty_batch_is_noop(lib):
+    # zero tokens: valid and nothing to do, so nothing is launched
+    assert lib.sattn_window_fwd(ctypes.byref(_window(total_tokens=0, q=None)), None) == OK
+
+
+def _indexed(**kw):
+    base = dict(dtype=0, q=FAKE, kv=FAKE, topk_idxs=FAKE, o=FAKE, lse=None, batch=1, q_len=4, num_heads=32,
+                head_dim=128, kv_len=100, topk=64, softmax_scale=0.1, sinks=None, sink_mode=0, num_splits=1,
+                workspace=None, workspace_bytes=0)
+    base.update(kw)
+    return _IndexedArgs(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=2), DTYPE),
+    (dict(sink_mode=2, sinks=None), NULL_PTR),
+    (dict(num_splits=0), ARG),
+    (dict(num_splits=65), ARG),
+    (dict(topk=-1), SHAPE),
+    (dict(kv_len=-5), SHAPE),
+    (dict(head_dim=100), UNSUPPORTED),
+    (dict(q=None), NULL_PTR),
+    (dict(topk_idxs=None), NULL_PTR),
+    (dict(kv=FAKE + 4), ALIGNMENT),
+    (dict(num_splits=4), WORKSPACE),
+    (dict(num_splits=4, workspace=FAKE, workspace_bytes=16), WORKSPACE),
+    (dict(num_splits=4, workspace=FAKE + 16, workspace_bytes=1 << 30), WORKSPACE),
+])
+def test_indexed_validation(lib, kw, status):
+    assert lib.sattn_indexed_fwd(ctypes.byref(_indexed(**kw)), None) == status
+
+
+def test_indexed_empty_is_noop(lib):
+    assert lib.sattn_indexed_fwd(ctypes.byref(_indexed(q_len=0, q=None)), None) == OK
+
+
+def _merge(**kw):
+    base = dict(part_o=FAKE, part_lse=FAKE, num_parts=8, rows=64, num_heads=64, head_dim=128, sinks=None,
+                sink_mode=0, out_dtype=0, o=FAKE, lse=None)
+    base.update(kw)
+    return _MergeArgs(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(sink_mode=1, sinks=FAKE), ARG),
+    (dict(sink_mode=2, sinks=None), NULL_PTR),
+    (dict(out_dtype=3), DTYPE),
+    (dict(num_parts=-1), SHAPE),
+    (dict(part_o=None), NULL_PTR),
+    (dict(o=FAKE + 4), ALIGNMENT),
+])
+def test_merge_validation(lib, kw, status):
+    assert lib.sattn_merge_lse(ctypes.byref(_merge(**kw)), None) == status

@@ -1,0 +1,257 @@
+"""GPU parity: libsattn (through its C ABI) against the CPU oracle, element by element.
+
+Reduced versions of the five workloads are compared on every output element;
+the full-size workloads, launched exactly as bench.py times them, are compared
+on sampled query rows the oracle evaluates one by one.  Edge cases cover what
+the pages flag as risks: windows narrower than a key block, tiles that start
+at a sequence boundary (key-0 placement), length-1 and empty sequences,
+all-padding index lists, split counts that leave empty slices, and a
+non-default stream fed through an event.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sliding_window_attention_index_amd as sattn
+import workloads as W
+from parity import (check_indexed, check_window, compare, oracle_indexed, oracle_window, run_indexed, run_window,
+                    sample_rows)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    sattn.load_library()  # fails loudly if the HIP library is missing
+    return torch.device("cuda:0")
+
+
+def _log(name, res):
+    print(f"[parity] {name}: {res}", flush=True)
+
+
+# ---------------------------------------------------------------------------
+# window path
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kv_heads", [4, 2])
+def test_tiny_window_fp32(dev, kv_heads):
+    """The page's own test shape: lengths 5 and 37, window 8, 4 heads, key-0 sinks, fp32."""
+    case = W.tiny_window_fp32(kv_heads)
+    _log(case.name, check_window(case, dev))
+
+
+WINDOW_CASES = [
+    # name, lens, H, Hkv, D, (wl, wr), sink mode, dtype
+    ("vision_reduced", [300, 1, 517, 64, 129], 16, 8, 128, (128, 128), W.SINK_KEY0, torch.bfloat16),
+    ("causal_null_reduced", [700, 333], 64, 8, 64, (127, 0), W.SINK_NULL, torch.bfloat16),
+    ("narrow_window", [70, 3, 45], 8, 2, 128, (3, 2), W.SINK_KEY0, torch.bfloat16),
+    ("full_noncausal", [90, 17], 4, 4, 64, (-1, -1), W.SINK_NONE, torch.bfloat16),
+    ("full_causal", [150], 8, 1, 64, (-1, 0), W.SINK_NULL, torch.bfloat16),
+    ("left_only_unbounded", [100], 32, 1, 128, (-1, 5), W.SINK_KEY0, torch.bfloat16),
+    ("gqa16", [80, 40], 16, 1, 128, (20, 20), W.SINK_NONE, torch.bfloat16),
+    ("gqa32", [50], 32, 1, 64, (10, 0), W.SINK_NULL, torch.bfloat16),
+    ("gqa4_d64", [200, 33], 16, 4, 64, (64, 64), W.SINK_KEY0, torch.bfloat16),
+    ("empty_seqs", [0, 40, 0, 1, 0], 4, 2, 64, (8, 8), W.SINK_KEY0, torch.bfloat16),
+    ("valu_gqa3", [60, 9], 6, 2, 64, (7, 7), W.SINK_KEY0, torch.bfloat16),
+    ("valu_d96", [45], 4, 2, 96, (5, 5), W.SINK_NULL, torch.bfloat16),
+    ("valu_d256", [33], 2, 1, 256, (4, 4), W.SINK_KEY0, torch.bfloat16),
+    ("fp32_vision", [129, 64], 16, 8, 128, (128, 128), W.SINK_KEY0, torch.float32),
+    ("fp32_causal_null", [100], 16, 2, 64, (31, 0), W.SINK_NULL, torch.float32),
+    ("fp32_none", [70, 1], 4, 4, 32, (-1, -1), W.SINK_NONE, torch.float32),
+]
+
+
+@pytest.mark.parametrize("spec", WINDOW_CASES, ids=[c[0] for c in WINDOW_CASES])
+def test_window_cases(dev, spec):
+    name, lens, H, Hkv, D, (wl, wr), mode, dt = spec
+    case = W.make_window_case(name, lens, H, Hkv, D, wl, wr, mode, dtype=dt, seed=7)
+    _log(name, check_window(case, dev))
+
+
+def test_window_sink_bit_exact_invariants(dev):
+    """Key-0 sink 0 == no sink and null sink -inf == no sink, bit for bit on the GPU as well."""
+    base = W.make_window_case("inv", [200, 77], 16, 8, 128, 128, 128, W.SINK_NONE, seed=3)
+    o0 = run_window(base, dev, return_lse=False)
+    for mode, val in ((W.SINK_KEY0, 0.0), (W.SINK_NULL, -math.inf)):
+        c = W.make_window_case("inv", [200, 77], 16, 8, 128, 128, 128, mode, seed=3, sinks_value=val)
+        assert torch.equal(c.q, base.q)
+        o1 = run_window(c, dev, return_lse=False)
+        assert torch.equal(o0, o1), f"sink mode {mode} with neutral value changed the output"
+
+
+def test_window_max_seqlen_bounds_work(dev):
+    """Tokens beyond max_seqlen are not computed (the grid is sized by it, as the page's max_input_len)."""
+    case = W.make_window_case("bound", [64, 40], 8, 2, 128, 8, 8, W.SINK_NONE, seed=4)
+    q, k, v = (t.to(dev) for t in (case.q, case.k, case.v))
+    out = torch.full_like(q, 7.0)
+    sattn.window_fwd(q, k, v, case.cu_seqlens.to(dev), 40, window=(8, 8), out=out)
+    torch.cuda.synchronize()
+    ro, _ = oracle_window(case)
+    o = out.cpu()
+    compare(o[:40], ro[:40], torch.bfloat16, "first 40 of seq 0")
+    compare(o[64:], ro[64:], torch.bfloat16, "seq 1")
+    assert torch.all(o[40:64] == 7.0)
+
+
+def test_vision_window_full_size_sampled(dev):
+    """16 sequences, lengths U[1024,4096], 16/8 heads, D=128, window +-128, key-0 sinks (bench workload)."""
+    case = W.vision_window()
+    cu = case.cu_seqlens.numpy()
+    must = list(cu[:-1]) + list(cu[1:] - 1) + list(cu[:-1] + 63) + list(cu[:-1] + 64) + list(cu[:-1] + 200)
+    rows = sample_rows(int(cu[-1]), 192, seed=1, must=must)
+    _log("vision_window full (sampled)", check_window(case, dev, rows=rows))
+
+
+def test_causal_window_full_size_sampled(dev):
+    """4 x 8192 tokens, 64/8 heads, D=64, causal 128-key window, null sinks."""
+    case = W.causal_window_null()
+    cu = case.cu_seqlens.numpy()
+    must = list(cu[:-1]) + list(cu[1:] - 1) + list(cu[:-1] + 127) + list(cu[:-1] + 128)
+    rows = sample_rows(int(cu[-1]), 160, seed=2, must=must)
+    _log("causal_window_null full (sampled)", check_window(case, dev, rows=rows))
+
+
+# ---------------------------------------------------------------------------
+# indexed path
+# ---------------------------------------------------------------------------
+
+def test_sparse_prefill_reduced_with_padding(dev):
+    """Top-k prefill, queries at positions 0.. (short lists padded with -1), 32 heads, D=128."""
+    case = W.sparse_prefill_case(q_len=300, total_tokens=4096, n_pick=64, first_pos=0, name="prefill_pad")
+    _log(case.name, check_indexed(case, dev))
+
+
+def test_sparse_prefill_reduced_tail(dev):
+    case = W.sparse_prefill_case(q_len=256, total_tokens=4096, n_pick=96, name="prefill_tail")
+    _log(case.name, check_indexed(case, dev))
+
+
+@pytest.mark.parametrize("mode", [W.SINK_KEY0, W.SINK_NULL])
+def test_sparse_prefill_sinks(dev, mode):
+    """Window ring slot 0 is cache row 0, so the key-0 bias is exercised by many lists."""
+    case = W.sparse_prefill_case(q_len=200, total_tokens=2048, n_pick=40, first_pos=100, sink_mode=mode,
+                                 name=f"prefill_sink{mode}")
+    _log(case.name, check_indexed(case, dev))
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 8, 19])
+@pytest.mark.parametrize("mode", [W.SINK_NONE, W.SINK_NULL, W.SINK_KEY0])
+def test_sparse_decode_reduced_splits(dev, splits, mode):
+    """Decode: 4 sequences x 1 query, 64 heads sharing one cache row per token, split-K + merge."""
+    case = W.sparse_decode_case(batch=4, total_tokens=8192, n_pick=480, num_splits=splits, sink_mode=mode,
+                                name=f"decode_s{splits}_m{mode}")
+    _log(case.name, check_indexed(case, dev))
+
+
+INDEXED_EDGE = [
+    # name, B, M, H, D, N, K, pad pattern, dtype, splits
+    ("all_pad", 1, 3, 32, 128, 50, 40, "all", torch.bfloat16, 1),
+    ("all_pad_split", 1, 3, 64, 128, 50, 40, "all", torch.bfloat16, 4),
+    ("ragged_k", 2, 5, 32, 64, 300, 45, "some", torch.bfloat16, 1),
+    ("k1", 1, 4, 32, 128, 10, 1, "none", torch.bfloat16, 1),
+    ("out_of_range", 1, 4, 32, 128, 64, 40, "oob", torch.bfloat16, 1),
+    ("empty_cache", 1, 2, 32, 128, 0, 8, "all", torch.bfloat16, 1),
+    ("valu_h16", 2, 3, 16, 128, 200, 70, "some", torch.bfloat16, 1),
+    ("valu_h16_split", 2, 3, 16, 64, 200, 70, "some", torch.bfloat16, 3),
+    ("fp32", 1, 6, 32, 128, 200, 64, "some", torch.float32, 1),
+    ("fp32_split", 1, 6, 8, 64, 200, 64, "some", torch.float32, 4),
+]
+
+
+def _edge_lists(rng, B, M, N, K, pattern):
+    idx = np.full((B, M, K), -1, np.int32)
+    for b in range(B):
+        for t in range(M):
+            if pattern == "all" or N == 0:
+                continue
+            n = K if pattern == "none" else int(rng.integers(0, min(K, N) + 1))
+            n = min(n, N)
+            idx[b, t, :n] = rng.choice(N, size=n, replace=False)
+            if pattern == "some":
+                idx[b, t] = idx[b, t, rng.permutation(K)]
+            if pattern == "oob":
+                idx[b, t, ::7] = N + 3 + t  # outside the cache: must be ignored
+    return idx
+
+
+@pytest.mark.parametrize("spec", INDEXED_EDGE, ids=[c[0] for c in INDEXED_EDGE])
+@pytest.mark.parametrize("mode", [W.SINK_NONE, W.SINK_KEY0, W.SINK_NULL])
+def test_indexed_edge_cases(dev, spec, mode):
+    name, B, M, H, D, N, K, pattern, dt, splits = spec
+    rng = np.random.default_rng(5)
+    idx = _edge_lists(rng, B, M, N, K, pattern)
+    if mode == W.SINK_KEY0 and N > 0 and pattern != "all":
+        idx[0, 0, 0] = 0 if 0 not in idx[0, 0] else idx[0, 0, 0]
+    case = W.make_indexed_case(f"{name}_m{mode}", B, M, H, D, N, idx, mode, dtype=dt, seed=9, num_splits=splits)
+    _log(case.name, check_indexed(case, dev))
+
+
+def test_indexed_padding_bit_exact(dev):
+    """Appending -1 padding leaves the single-pass result bit-identical."""
+    case = W.sparse_prefill_case(q_len=64, total_tokens=2048, n_pick=32, name="pad_inv")
+    o0 = run_indexed(case, dev, return_lse=False)
+    padded = torch.cat([case.topk_idxs, torch.full((1, 64, 40), -1, dtype=torch.int32)], 2).contiguous()
+    o1 = run_indexed(case, dev, idx=padded, return_lse=False)
+    assert torch.equal(o0, o1)
+
+
+def test_sparse_prefill_full_size_sampled(dev):
+    """8192 queries x 32 heads x 640 listed rows of a 8320-row shared cache (as timed by the bench)."""
+    case = W.sparse_prefill_case()
+    rows = sample_rows(case.q.shape[1], 128, seed=3, must=[0, 1, 8191])
+    _log("sparse_prefill full (sampled)", check_indexed(case, dev, rows=rows))
+
+
+def test_sparse_decode_full_size_sampled(dev):
+    """64 decode queries x 64 heads, 2048-entry lists over 32896-row caches, 8 splits + merge."""
+    case = W.sparse_decode_case()
+    rows = sample_rows(64, 24, seed=4, must=[0, 63])
+    _log("sparse_decode full (sampled)", check_indexed(case, dev, rows=rows))
+
+
+# ---------------------------------------------------------------------------
+# merge and streams
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mode", [W.SINK_NONE, W.SINK_NULL])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_merge_lse_parity(dev, mode, out_dtype):
+    g = torch.Generator().manual_seed(12)
+    S, R, H, D = 5, 37, 8, 128
+    po = torch.randn(S, R, H, D, generator=g)
+    pl = torch.randn(S, R, H, generator=g) * 3
+    pl[2, :5] = -math.inf
+    pl[:, 7, 3] = -math.inf
+    sinks = torch.randn(H, generator=g)
+    o, lse = sattn.merge_lse(po.to(dev), pl.to(dev), sinks=sinks.to(dev), sink_mode=("none", "key0", "null")[mode],
+                             out_dtype=out_dtype, return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.merge(po, pl, sinks=sinks, sink_mode=mode)
+    compare(o.cpu(), ro, out_dtype, "merge o")
+    compare(lse.cpu(), rl, torch.float32, "merge lse", lse=True)
+
+
+def test_non_default_stream_with_event(dev):
+    """Inputs produced on one stream, the call made on another that waits on an event (no default stream)."""
+    case = W.make_window_case("stream", [900, 300], 16, 8, 128, 128, 128, W.SINK_KEY0, seed=8)
+    q_host, k_host, v_host = (t.pin_memory() for t in (case.q, case.k, case.v))
+    producer, consumer = torch.cuda.Stream(), torch.cuda.Stream()
+    with torch.cuda.stream(producer):
+        q = q_host.to(dev, non_blocking=True)
+        k = k_host.to(dev, non_blocking=True)
+        v = v_host.to(dev, non_blocking=True)
+        cu = case.cu_seqlens.to(dev, non_blocking=True)
+        sinks = case.sinks.to(dev, non_blocking=True)
+        ready = torch.cuda.Event()
+        ready.record(producer)
+    consumer.wait_event(ready)
+    with torch.cuda.stream(consumer):
+        o = sattn.window_fwd(q, k, v, cu, case.max_seqlen, window=(128, 128), sinks=sinks, sink_mode="key0")
+    consumer.synchronize()
+    ro, _ = oracle_window(case)
+    compare(o.cpu(), ro, torch.bfloat16, "stream o")
