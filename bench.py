@@ -1,0 +1,338 @@
+"""Benchmark: attended query-key pairs per second of libsattn on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu] [--no-extra]
+
+One step is one call of the hot path on one batch of synthetic input that is
+already resident in HBM.  The headline workload is the vision-encoder window
+attention (16 sequences, lengths U[1024, 4096], 16 query / 8 KV heads,
+head_dim 128, symmetric window 128, key-0 sinks, bf16).  The other workloads
+(causal window with null sinks, top-k prefill over a shared K=V cache, top-k
+decode with split-K and merge) are timed the same way and reported inside the
+same JSON line under "workloads".
+
+To keep the 256 MB last-level cache (MALL) from serving a step's inputs from
+the previous step, every workload rotates between input sets whose union is
+larger than the MALL.
+
+Roofline: algorithmic bytes (each q/k/v/o element once for the window path;
+each listed cache row once per query, plus q/o/index lists, for the top-k
+path) or algorithmic flops (4 * head_dim per attended pair) per launch,
+divided by the kernel time measured with events on the launch stream.
+The CPU baseline times the oracle (plain C, fp64, OpenMP) on a bounded sample
+of query tokens of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def _src_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sliding_window_attention_index_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they match the current kernels."""
+    path = os.path.join(PROFILES, f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha") != _src_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+class Workload:
+    name: str
+    bound: str
+
+    def __init__(self, device):
+        self.device = device
+
+    def launch(self, i: int):
+        raise NotImplementedError
+
+
+def _window_sets(make, n_sets, device):
+    import torch
+    sets = []
+    for s in range(n_sets):
+        c = make(s)
+        sets.append(dict(case=c, q=c.q.to(device), k=c.k.to(device), v=c.v.to(device),
+                         cu=c.cu_seqlens.to(device), sinks=None if c.sinks is None else c.sinks.to(device),
+                         o=torch.empty_like(c.q, device=device)))
+    return sets
+
+
+class WindowWorkload(Workload):
+    def __init__(self, device, name, make, n_sets=2):
+        super().__init__(device)
+        self.name = name
+        self.bound = "hbm"
+        self.sets = _window_sets(make, n_sets, device)
+        c0 = self.sets[0]["case"]
+        T, H, Hkv, D = c0.dims
+        # identical lengths across sets (same seed for lengths), so pairs and bytes are per-set constants
+        self.pairs = c0.pairs()
+        self.bytes = T * (2 * H * D + 2 * Hkv * D) * 2
+        self.flops = 4 * D * self.pairs
+        self.config = dict(workload=name, tokens=T, num_seqs=int(c0.cu_seqlens.numel() - 1), num_heads=H,
+                           num_kv_heads=Hkv, head_dim=D, window=[c0.window_left, c0.window_right],
+                           sink_mode=["none", "key0", "null"][c0.sink_mode])
+        self.case0 = c0
+
+    def launch(self, i):
+        import sliding_window_attention_index_amd as sattn
+        s = self.sets[i % len(self.sets)]
+        c = s["case"]
+        sattn.window_fwd(s["q"], s["k"], s["v"], s["cu"], c.max_seqlen, window=(c.window_left, c.window_right),
+                         softmax_scale=c.scale, sinks=s["sinks"], sink_mode=["none", "key0", "null"][c.sink_mode],
+                         out=s["o"])
+
+
+class IndexedWorkload(Workload):
+    def __init__(self, device, name, case, idx_sets, q_sets=1, bound="hbm"):
+        import torch
+        super().__init__(device)
+        self.name = name
+        self.bound = bound
+        self.case0 = case
+        self.kv = case.kv.to(device)
+        g = torch.Generator().manual_seed(1234)
+        self.qs = [case.q.to(device)] + [torch.randn(case.q.shape, generator=g).to(case.q.dtype).to(device)
+                                         for _ in range(q_sets - 1)]
+        self.idx = [t.to(device) for t in idx_sets]
+        self.o = [torch.empty_like(q) for q in self.qs]
+        self.sinks = None if case.sinks is None else case.sinks.to(device)
+        B, M, H, D, N, K = case.dims
+        self.workspace = None
+        import sliding_window_attention_index_amd as sattn
+        wsb = sattn.indexed_workspace_size(B, M, H, D, case.num_splits)
+        if wsb:
+            self.workspace = torch.empty(wsb, dtype=torch.uint8, device=device)
+        valid = [int(((t >= 0) & (t < N)).sum()) for t in idx_sets]
+        self.pairs = valid[0] * H
+        self.bytes = valid[0] * D * 2 + 2 * B * M * H * D * 2 + B * M * K * 4
+        self.flops = 4 * D * self.pairs
+        self.config = dict(workload=name, batch=B, q_len=M, num_heads=H, head_dim=D, kv_len=N, topk=K,
+                           num_splits=case.num_splits, sink_mode=["none", "key0", "null"][case.sink_mode],
+                           index_sets=len(self.idx))
+
+    def launch(self, i):
+        import sliding_window_attention_index_amd as sattn
+        c = self.case0
+        j = i % len(self.qs)
+        sattn.indexed_fwd(self.qs[j], self.kv, self.idx[i % len(self.idx)], softmax_scale=c.scale, sinks=self.sinks,
+                          sink_mode=["none", "key0", "null"][c.sink_mode], num_splits=c.num_splits, out=self.o[j],
+                          workspace=self.workspace)
+
+
+def build_workload(name, device):
+    import workloads as W
+    if name == "vision_window":
+        return WindowWorkload(device, name, lambda s: W.vision_window(seed=0) if s == 0 else _reseed_window(
+            W.vision_window(seed=0), s))
+    if name == "causal_window_null":
+        return WindowWorkload(device, name, lambda s: W.causal_window_null(seed=s))
+    if name == "sparse_prefill":
+        c = W.sparse_prefill_case(seed=0)
+        return IndexedWorkload(device, name, c, [c.topk_idxs], q_sets=3, bound="mfma")
+    if name == "sparse_decode":
+        c = W.sparse_decode_case(seed=0, index_sets=16)
+        return IndexedWorkload(device, name, c, c.extra["idx_sets"], q_sets=1, bound="hbm")
+    raise ValueError(name)
+
+
+def _reseed_window(case, s):
+    """Same lengths (pair count and bytes unchanged), fresh q/k/v values for input set s."""
+    import torch
+    g = torch.Generator().manual_seed(1000 + s)
+    for attr in ("q", "k", "v"):
+        t = getattr(case, attr)
+        setattr(case, attr, torch.randn(t.shape, generator=g).to(t.dtype))
+    return case
+
+
+def time_workload(wl, steps, warmup):
+    """Wall time of `steps` launches (synchronised on both sides) and the mean per-launch event time."""
+    import torch
+    for i in range(warmup):
+        wl.launch(i)
+    torch.cuda.synchronize()
+    # per-launch durations from events on the launch stream (torch's current stream)
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        evs[i][0].record(stream)
+        wl.launch(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    mean_ev = sum(ev_ms) / len(ev_ms)
+    return wall, mean_ev, ev_ms[len(ev_ms) // 2]
+
+
+def roofline(wl, kernel_ms):
+    sec = kernel_ms / 1e3
+    if wl.bound == "mfma":
+        ach = wl.flops / sec / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": _traffic(wl.name),
+                "algorithmic_flops_per_launch": wl.flops}
+    ach = wl.bytes / sec / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": _traffic(wl.name),
+            "algorithmic_bytes_per_launch": wl.bytes,
+            "mfma_tflops": round(wl.flops / sec / 1e12, 2)}
+
+
+def cpu_baseline(wl, budget_s=12.0):
+    """Oracle (fp64 C, OpenMP on all host cores) on a seeded sample of query tokens of the same workload."""
+    import numpy as np
+
+    import oracle
+    import workloads as W
+    c = wl.case0
+    rng = np.random.default_rng(0)
+    if isinstance(c, W.WindowCase):
+        T = c.q.shape[0]
+        cu = c.cu_seqlens.numpy()
+        lens = cu[1:] - cu[:-1]
+        seq_of = np.repeat(np.arange(len(lens)), lens)
+
+        def pairs_of(rows):
+            tot = 0
+            for t in rows:
+                s = seq_of[t]
+                i = t - cu[s]
+                L = lens[s]
+                lo = 0 if c.window_left < 0 else max(0, i - c.window_left)
+                hi = L - 1 if c.window_right < 0 else min(L - 1, i + c.window_right)
+                tot += max(0, hi - lo + 1)
+            return tot * c.q.shape[1]
+
+        def run(rows):
+            oracle.window(c.q, c.k, c.v, c.cu_seqlens, window_left=c.window_left, window_right=c.window_right,
+                          scale=c.scale, sinks=c.sinks, sink_mode=c.sink_mode, rows=rows)
+        total = T
+    else:
+        B, M = c.q.shape[:2]
+        N = c.kv.shape[1]
+        idx = c.topk_idxs.numpy().reshape(B * M, -1)
+
+        def pairs_of(rows):
+            return int(((idx[rows] >= 0) & (idx[rows] < N)).sum()) * c.q.shape[2]
+
+        def run(rows):
+            oracle.indexed(c.q, c.kv, c.topk_idxs, scale=c.scale, sinks=c.sinks, sink_mode=c.sink_mode, rows=rows)
+        total = B * M
+    probe = np.sort(rng.choice(total, size=min(total, 64), replace=False))
+    t0 = time.perf_counter()
+    run(probe)
+    dt = max(time.perf_counter() - t0, 1e-4)
+    n = int(min(total, max(64, 64 * budget_s / dt)))
+    rows = np.sort(rng.choice(total, size=n, replace=False))
+    # repeat the sample until about budget_s of CPU time has been measured
+    reps, dt = 0, 0.0
+    while dt < budget_s and reps < 100:
+        t0 = time.perf_counter()
+        run(rows)
+        dt += time.perf_counter() - t0
+        reps += 1
+    p = pairs_of(rows) * reps
+    n_desc = f"all {total}" if n == total else f"{n} of {total}"
+    return {"value": round(p / dt, 1), "unit": "pairs/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": f"{n_desc} query tokens (all heads) of {wl.name}, seeded, x{reps} passes; {p} pairs in {dt:.2f} s",
+            "seconds": round(dt, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="vision_window",
+                    choices=["vision_window", "causal_window_null", "sparse_prefill", "sparse_decode"])
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-extra", action="store_true", help="time only the headline workload")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the path shards "
+              "without exchange by sequence, query or batch row, so N GPUs run N independent copies.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sliding_window_attention_index_amd as sattn
+    sattn.load_library()
+    dev = torch.device("cuda:0")
+
+    names = [args.workload]
+    if not args.no_extra:
+        names += [n for n in ("vision_window", "causal_window_null", "sparse_prefill", "sparse_decode")
+                  if n != args.workload]
+    results = {}
+    main_wl = None
+    for name in names:
+        print(f"[bench] preparing {name}", file=sys.stderr, flush=True)
+        wl = build_workload(name, dev)
+        steps = args.steps
+        wall, mean_ev, med_ev = time_workload(wl, steps, args.warmup)
+        ms = wall / steps * 1e3
+        rec = {"value": round(wl.pairs / (ms / 1e3), 1), "unit": "pairs/s", "ms_per_step": round(ms, 5),
+               "kernel_ms_mean": round(mean_ev, 5), "kernel_ms_median": round(med_ev, 5), "pairs": wl.pairs,
+               "config": wl.config, "roofline": roofline(wl, mean_ev)}
+        print(f"[bench] {name}: {json.dumps(rec)}", file=sys.stderr, flush=True)
+        results[name] = rec
+        if name == args.workload:
+            main_wl = wl
+        else:
+            del wl
+            torch.cuda.empty_cache()
+
+    head = results[args.workload]
+    line = {
+        "metric": "attended q-k pairs/sec",
+        "value": head["value"],
+        "unit": "pairs/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": head["config"],
+        "roofline": head["roofline"],
+        "cpu_baseline": None if args.no_cpu else cpu_baseline(main_wl),
+        "workloads": {k: v for k, v in results.items() if k != args.workload},
+        "kernel_source_sha": _src_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
