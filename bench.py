@@ -276,6 +276,8 @@ def main():
                     choices=["vision_window", "causal_window_null", "sparse_prefill", "sparse_decode"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-extra", action="store_true", help="time only the headline workload")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 256 MiB device-to-device copy 5 times (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the path shards "
@@ -284,9 +286,18 @@ def main():
         sys.exit(2)
 
     import torch
+    dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        n = 256 << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "copies": 5}), flush=True)
+        return
     import sliding_window_attention_index_amd as sattn
     sattn.load_library()
-    dev = torch.device("cuda:0")
 
     names = [args.workload]
     if not args.no_extra:

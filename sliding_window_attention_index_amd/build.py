@@ -23,7 +23,13 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["sattn_api.cpp", "valu_fwd.hip", "indexed_mfma.hip", "window_mfma.hip"]
-HEADERS = ["sattn_device.hpp", "sattn_kernels.hpp"]
+HEADERS = ["sattn_device.hpp", "sattn_kernels.hpp", "softmax_block.hpp", "lds_tile.hpp"]
+# MFMA kernels keep their accumulators in VGPRs: the online-softmax rescale is a VALU
+# multiply, which cannot read AGPRs and would otherwise copy the accumulator every block.
+EXTRA_FLAGS = {
+    "indexed_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "window_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}",
@@ -43,6 +49,7 @@ def _compile(src: str, verbose: bool) -> str:
     cmd = [HIPCC, *COMMON_FLAGS]
     if src.endswith(".cpp"):
         cmd += ["-x", "hip"]
+    cmd += EXTRA_FLAGS.get(src, [])
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)

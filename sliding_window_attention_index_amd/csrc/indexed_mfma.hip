@@ -30,13 +30,13 @@
 //   * Gathers for block b+1 are issued before block b is computed.
 #include "sattn_device.hpp"
 #include "sattn_kernels.hpp"
+#include "softmax_block.hpp"
 
 namespace sattn {
 namespace {
 
 constexpr int kBlockKeys = 32;
 constexpr int kPad = 16;  // LDS row padding (bf16 elements): keeps the transposed reads conflict-free
-constexpr float kRescaleThreshold = 8.0f;
 
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -84,18 +84,19 @@ __global__ __launch_bounds__(256) void indexed_fwd_mfma(IndexedParams p) {
 #pragma unroll
       for (int s = 0; s < S; ++s) qf[hb][s] = *reinterpret_cast<const bf16x8 *>(qrow + hb * 32 * D + s * 8);
   }
-  float sink2[HB];
+  const float c = p.scale_log2;  // > 0 on this path
+  float sink_raw[HB];  // sink in raw logit units (the running max is kept unscaled)
 #pragma unroll
-  for (int hb = 0; hb < HB; ++hb) sink2[hb] = p.sinks ? p.sinks[head0 + hb * 32 + n] * kLog2e : 0.0f;
+  for (int hb = 0; hb < HB; ++hb) sink_raw[hb] = p.sinks ? p.sinks[head0 + hb * 32 + n] * kLog2e / c : 0.0f;
 
   f32x16 acc[HB][DB];
-  float m_run[HB], l_part[HB];
+  RowSoftmax rs[HB];
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[hb][db] = f32x16{};
-    m_run[hb] = null_sink ? sink2[hb] : kNegInf;
-    l_part[hb] = (null_sink && h == 0) ? 1.0f : 0.0f;  // the pair of lanes sharing a head splits l
+    rs[hb].m = null_sink ? sink_raw[hb] : kNegInf;
+    rs[hb].l = (null_sink && h == 0) ? 1.0f : 0.0f;  // the pair of lanes sharing a head splits l
   }
 
   const int kb = part * p.part_len;
@@ -143,58 +144,16 @@ __global__ __launch_bounds__(256) void indexed_fwd_mfma(IndexedParams p) {
       }
       // Accumulator element r of lane (n, h) is key 8*(r/4) + 4h + r%4 of head n.
       bf16x8 pb[HB][2];
-      float t[HB][16];
-      float m_new[HB];
-      bool grow = false;
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) t[hb][r] = st[hb][r] * p.scale_log2;
-        if (zmask) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = 8 * (r >> 2) + 4 * h + (r & 3);
-            if ((zmask >> key) & 1u) t[hb][r] += sink2[hb];
-          }
-        }
-        if (vmask != 0xffffffffu) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = 8 * (r >> 2) + 4 * h + (r & 3);
-            if (!((vmask >> key) & 1u)) t[hb][r] = kNegInf;
-          }
-        }
-        float bm = t[hb][0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) bm = fmaxf(bm, t[hb][r]);
-        m_new[hb] = fmaxf(m_run[hb], halves_max(bm));
-        grow |= m_new[hb] > m_run[hb] + kRescaleThreshold;
-      }
-      if (__ballot(grow)) {
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb) {
-          const float alpha = fast_exp2(m_run[hb] - m_new[hb]);
-          l_part[hb] *= alpha;
+        if (zmask) bias_block(st[hb], zmask, h, sink_raw[hb]);
+        if (vmask != 0xffffffffu) mask_block(st[hb], vmask, h);
+        float alpha;
+        if (softmax_need_rescale(rs[hb], block_max(st[hb]), c, alpha)) {
 #pragma unroll
           for (int db = 0; db < DB; ++db) acc[hb][db] *= alpha;
-          m_run[hb] = m_new[hb];
         }
-      }
-#pragma unroll
-      for (int hb = 0; hb < HB; ++hb) {
-        const float mref = m_run[hb] == kNegInf ? 0.0f : m_run[hb];
-        float e[16];
-        float ps = 0.0f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          e[r] = fast_exp2(t[hb][r] - mref);
-          ps += e[r];
-        }
-        l_part[hb] += ps;
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) pb[hb][tt][j] = static_cast<__bf16>(e[8 * tt + j]);
+        softmax_probs(st[hb], rs[hb], c, pb[hb]);
       }
 
       wave_lds_sync();
@@ -225,9 +184,9 @@ __global__ __launch_bounds__(256) void indexed_fwd_mfma(IndexedParams p) {
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) {
     const int head = head0 + hb * 32 + n;
-    const float l_tot = halves_sum(l_part[hb]);
+    const float l_tot = halves_sum(rs[hb].l);
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    const float lse_v = l_tot > 0.0f ? (m_run[hb] + log2f(l_tot)) * kLn2 : kNegInf;
+    const float lse_v = l_tot > 0.0f ? (rs[hb].m * c + log2f(l_tot)) * kLn2 : kNegInf;
     if (partial) {
       const int64_t row = (static_cast<int64_t>(part) * BM + bt) * H + head;
       float *dst = p.part_o + row * D + 4 * h;
@@ -270,7 +229,7 @@ hipError_t launch(const IndexedParams &p, hipStream_t stream) {
 }  // namespace
 
 bool indexed_mfma_supported(const IndexedParams &p) {
-  return (p.head_dim == 64 || p.head_dim == 128) && p.num_heads % 32 == 0;
+  return p.scale_log2 > 0.0f && (p.head_dim == 64 || p.head_dim == 128) && p.num_heads % 32 == 0;
 }
 
 hipError_t launch_indexed_mfma(const IndexedParams &p, hipStream_t stream) {
