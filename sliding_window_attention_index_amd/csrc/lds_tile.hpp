@@ -89,6 +89,12 @@ __device__ __forceinline__ u32x2 ds_read_tr_b16(uint32_t addr) {
   asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
   return r;
 }
+// LDS write the compiler does not see (for wave-private staging next to DMA buffers).  A wave's
+// LDS instructions execute in order, so a later ds_read of the same bytes by this wave sees it.
+template <int OFF>
+__device__ __forceinline__ void ds_write_b128(uint32_t addr, u32x4 v) {
+  asm volatile("ds_write_b128 %0, %1 offset:%2" ::"v"(addr), "v"(v), "i"(OFF));
+}
 // s_waitcnt lgkmcnt(N) that the registers in `regs` depend on.
 template <int N, typename T, int M>
 __device__ __forceinline__ void lgkm_fence(T (&regs)[M]) {

@@ -84,12 +84,14 @@ __global__ __launch_bounds__(256) void window_fwd_mfma(WindowParams p) {
   constexpr int DPW = Tile::kDmaPerTile / 4;  // DMA instructions per wave per 32-row tile
   constexpr int kSlot = 2 * Tile::kBytes;     // K tile + V tile (or two Q half-tiles)
   constexpr int kDmaPerSlot = 2 * DPW;        // DMA instructions per wave per slot
-  constexpr int kStores = 4 * DB + 1;         // O stores + one lse store per wave per tile
+  constexpr int kStageBytes = 32 * 128;       // O staging per wave: 32 rows x 32 dims of fp32
+  constexpr int kStores = 2 * DB + 1;         // O stores + one lse store per wave per tile
   static_assert(DPW >= 1, "tile too small for four waves");
   static_assert(64 % G == 0, "a Q slot must hold whole queries");
   __shared__ __attribute__((aligned(1024))) char ring[kRing * kSlot];
+  __shared__ __attribute__((aligned(16))) char stage[4 * kStageBytes];
 
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar registers
   const int lane = lane_id();
   const int h = lane >> 5, n = lane & 31;
   const int H = p.num_heads, Hkv = p.num_kv_heads;
@@ -238,8 +240,14 @@ __global__ __launch_bounds__(256) void window_fwd_mfma(WindowParams p) {
     float sink = 0.0f;
     if (p.sink_mode != kSinkNone) sink = H <= 64 ? __shfl(sink_lane, head, 64) : p.sinks[head];
     sink_raw = sink * kLog2e / c;  // the running max is kept in raw logit units
+    // An opaque zero: a plain f32x16{} is loop invariant, and the compiler keeps it in 16 AGPRs
+    // across the whole persistent loop, which costs the kernel its second wave per SIMD.
+    float z = 0.0f;
+    asm volatile("" : "+v"(z));
 #pragma unroll
-    for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[db][r] = z;
     rs.m = p.sink_mode == kSinkNull ? sink_raw : kNegInf;
     rs.l = (p.sink_mode == kSinkNull && h == 0) ? 1.0f : 0.0f;  // the lane pair of a row splits l
   };
@@ -305,24 +313,53 @@ __global__ __launch_bounds__(256) void window_fwd_mfma(WindowParams p) {
       }
   };
 
-  // O and lse of the tile: buffer stores, always kStores instructions per wave (rows past the
-  // sequence fall outside the buffer and are dropped, as is the lse of the upper half-wave).
+  // O and lse of the tile, always kStores buffer stores per wave (rows past the sequence fall
+  // outside the buffer and are dropped, as is the lse of the upper half-wave).  The O^T
+  // accumulator gives a lane 4-dim pieces of one row; stored as they are, every instruction
+  // would scatter 8-byte pieces over 32 rows.  Instead each 32-dim block of the accumulator goes
+  // through a wave-private LDS area as scaled fp32 (16-byte chunk c of row r at c ^ (r & 7):
+  // conflict free both ways), is read back as 8 consecutive dims per lane, rounded and stored as
+  // 16 bytes per lane, 64 contiguous bytes per row.
   auto store_tile = [&](TileInfo t) {
     const float l_tot = halves_sum(rs.l);
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     const int64_t row0 = static_cast<int64_t>(t.a) * H + t.g * G;  // first (token, head) row of the tile's group
     const __amdgpu_buffer_rsrc_t ors =
         make_rsrc(static_cast<__bf16 *>(p.o) + row0 * D, static_cast<uint32_t>(t.Lq - 1) * q_tok + G * D * 2);
-    const uint32_t obase = static_cast<uint32_t>(my_q) * q_tok + (n % G) * D * 2 + 8 * h;
+    const uint32_t sbase = lds_addr(stage) + wave * kStageBytes;
+    // write side: lane (n, h) holds dims 32 db + 8 j + 4 h .. +3 of row n = fp32 chunk 2 j + h
+    const uint32_t wr0 = sbase + n * 128;
+    // read side: lane l takes row 16 i + l / 4, fp32 chunks 2 (l % 4) and 2 (l % 4) + 1
+    const int rl = lane >> 2, q4 = lane & 3;
+    const uint32_t rd0 = sbase + rl * 128 + (((2 * q4) ^ (rl & 7)) << 4);
+    const uint32_t rd1 = sbase + rl * 128 + (((2 * q4 + 1) ^ (rl & 7)) << 4);
+    // Wave row r = 16 i + rl is query wq0 + r / G, head t.g * G + r % G; as G divides 16 or 16
+    // divides G, its byte offset splits into a lane part (row rl) and a uniform part (16 i).
+    const uint32_t vlane = static_cast<uint32_t>(rl / G) * q_tok + (rl % G) * D * 2 + q4 * 16;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bf16x4 v = {static_cast<__bf16>(acc[db][4 * i] * inv), static_cast<__bf16>(acc[db][4 * i + 1] * inv),
-                          static_cast<__bf16>(acc[db][4 * i + 2] * inv),
-                          static_cast<__bf16>(acc[db][4 * i + 3] * inv)};
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), ors, obase + (32 * db + 8 * i) * 2, 0, 0);
+      for (int j = 0; j < 4; ++j) {
+        // scaled here, where the lane still owns row n (after the transposition it does not)
+        const u32x4 w = {__float_as_uint(acc[db][4 * j] * inv), __float_as_uint(acc[db][4 * j + 1] * inv),
+                         __float_as_uint(acc[db][4 * j + 2] * inv), __float_as_uint(acc[db][4 * j + 3] * inv)};
+        ds_write_b128<0>(wr0 + (((2 * j + h) ^ (n & 7)) << 4), w);
       }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        u32x4 x[2];
+        x[0] = ds_read_b128<0>(rd0 + i * 2048);
+        x[1] = ds_read_b128<0>(rd1 + i * 2048);
+        lgkm_fence<0>(x);
+        const bf16x8 v = {static_cast<__bf16>(__uint_as_float(x[0][0])), static_cast<__bf16>(__uint_as_float(x[0][1])),
+                          static_cast<__bf16>(__uint_as_float(x[0][2])), static_cast<__bf16>(__uint_as_float(x[0][3])),
+                          static_cast<__bf16>(__uint_as_float(x[1][0])), static_cast<__bf16>(__uint_as_float(x[1][1])),
+                          static_cast<__bf16>(__uint_as_float(x[1][2])), static_cast<__bf16>(__uint_as_float(x[1][3]))};
+        const uint32_t uni = static_cast<uint32_t>(wq0 + (16 * i) / G) * q_tok + ((16 * i) % G) * D * 2 + db * 64;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ors, vlane,
+                                               __builtin_amdgcn_readfirstlane(uni), 0);
+      }
+    }
     const __amdgpu_buffer_rsrc_t lrs =
         make_rsrc(p.lse ? p.lse + row0 : nullptr, p.lse ? (static_cast<uint32_t>(t.Lq - 1) * H + G) * 4 : 0u);
     const float lse_v = l_tot > 0.0f ? (rs.m * c + log2f(l_tot)) * kLn2 : kNegInf;
