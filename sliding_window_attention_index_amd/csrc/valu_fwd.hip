@@ -177,6 +177,52 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void indexed_fwd_valu(IndexedP
 }
 
 // Merge of per-chunk partial results: M = max(lse_c, sink), W = sum exp(lse_c - M) [+ exp(sink - M)].
+// One thread per (row, head, 4 consecutive dims): the parts' log-sum-exps first (maximum, then
+// weights), then every part's 16-byte slice of o in flight together.  [P3] technical details:
+// per-chunk softmax statistics combined into global ones; the null sink enters the denominator
+// once.
+template <typename T>
+__global__ __launch_bounds__(256) void merge4_kernel(MergeParams p) {
+  const int D4 = p.head_dim / 4;
+  const int64_t RH = static_cast<int64_t>(p.rows) * p.num_heads;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (gid >= RH * D4) return;
+  const int64_t rh = gid / D4;
+  const int q = static_cast<int>(gid - rh * D4);
+  const int hh = static_cast<int>(rh % p.num_heads);
+  const int S = p.num_parts;
+  const bool null_sink = p.sink_mode == kSinkNull;
+  float M = null_sink ? p.sinks[hh] : kNegInf;
+#pragma unroll 8
+  for (int c = 0; c < S; ++c) M = fmaxf(M, p.part_lse[c * RH + rh]);
+  T *orow = static_cast<T *>(p.o) + rh * p.head_dim + 4 * q;
+  if (M == kNegInf) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) store_elem(orow + e, 0.0f);
+    if (p.lse && q == 0) p.lse[rh] = kNegInf;
+    return;
+  }
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  float W = null_sink ? expf(p.sinks[hh] - M) : 0.0f;
+  const float *o4 = p.part_o + rh * p.head_dim + 4 * q;
+#pragma unroll 8
+  for (int c = 0; c < S; ++c) {
+    const float w = expf(p.part_lse[c * RH + rh] - M);  // 0 for an empty part (lse = -inf)
+    const f32x4 v = *reinterpret_cast<const f32x4 *>(o4 + c * RH * p.head_dim);
+    W += w;
+    if (w > 0.0f) {  // an empty part contributes nothing, whatever its o holds
+      acc[0] = fmaf(w, v[0], acc[0]);
+      acc[1] = fmaf(w, v[1], acc[1]);
+      acc[2] = fmaf(w, v[2], acc[2]);
+      acc[3] = fmaf(w, v[3], acc[3]);
+    }
+  }
+  const float inv = 1.0f / W;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) store_elem(orow + e, acc[e] * inv);
+  if (p.lse && q == 0) p.lse[rh] = M + logf(W);
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   const int wave = threadIdx.x >> 6;
@@ -243,6 +289,18 @@ hipError_t launch_indexed_valu(const IndexedParams &p, int elem_type, hipStream_
 
 hipError_t launch_merge(const MergeParams &p, hipStream_t stream) {
   const int64_t RH = static_cast<int64_t>(p.rows) * p.num_heads;
+  const bool vec = (reinterpret_cast<uintptr_t>(p.part_o) & 15u) == 0;  // head_dim % 8 == 0 always
+  if (vec) {
+    const int64_t threads = RH * (p.head_dim / 4);
+    const int64_t blocks = (threads + 255) / 256;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const dim3 grid(static_cast<unsigned>(blocks));
+    if (p.out_type == kF32)
+      hipLaunchKernelGGL(merge4_kernel<float>, grid, dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL(merge4_kernel<__bf16>, grid, dim3(256), 0, stream, p);
+    return hipGetLastError();
+  }
   const dim3 grid(static_cast<unsigned>((RH + 3) / 4));
   if (p.out_type == kF32)
     hipLaunchKernelGGL(merge_kernel<float>, grid, dim3(256), 0, stream, p);
