@@ -192,30 +192,49 @@ __global__ __launch_bounds__(256) void merge4_kernel(MergeParams p) {
   const int hh = static_cast<int>(rh % p.num_heads);
   const int S = p.num_parts;
   const bool null_sink = p.sink_mode == kSinkNull;
-  float M = null_sink ? p.sinks[hh] : kNegInf;
-#pragma unroll 8
-  for (int c = 0; c < S; ++c) M = fmaxf(M, p.part_lse[c * RH + rh]);
   T *orow = static_cast<T *>(p.o) + rh * p.head_dim + 4 * q;
+  const float *o4 = p.part_o + rh * p.head_dim + 4 * q;
+  // One pass, eight parts at a time: every load of a group is issued before any is used, and the
+  // running (M, W, acc) is rescaled when a group raises the maximum.
+  float M = null_sink ? p.sinks[hh] : kNegInf;
+  float W = null_sink ? 1.0f : 0.0f;
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  constexpr int kG = 8;
+  for (int c0 = 0; c0 < S; c0 += kG) {
+    float lv[kG];
+    f32x4 ov[kG];
+#pragma unroll
+    for (int j = 0; j < kG; ++j) {
+      const int c = min(c0 + j, S - 1);  // a clamped duplicate is given weight 0 below
+      lv[j] = c0 + j < S ? p.part_lse[c * RH + rh] : kNegInf;
+      ov[j] = *reinterpret_cast<const f32x4 *>(o4 + c * RH * p.head_dim);
+    }
+    float gm = lv[0];
+#pragma unroll
+    for (int j = 1; j < kG; ++j) gm = fmaxf(gm, lv[j]);
+    if (gm > M) {  // new maximum: rescale what has been summed
+      const float r = M == kNegInf ? 0.0f : expf(M - gm);
+      W *= r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] *= r;
+      M = gm;
+    }
+    if (M == kNegInf) continue;
+#pragma unroll
+    for (int j = 0; j < kG; ++j) {
+      const float w = expf(lv[j] - M);  // 0 for an empty part (lse = -inf)
+      W += w;
+      if (w > 0.0f) {  // an empty part contributes nothing, whatever its o holds
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = fmaf(w, ov[j][e], acc[e]);
+      }
+    }
+  }
   if (M == kNegInf) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) store_elem(orow + e, 0.0f);
     if (p.lse && q == 0) p.lse[rh] = kNegInf;
     return;
-  }
-  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  float W = null_sink ? expf(p.sinks[hh] - M) : 0.0f;
-  const float *o4 = p.part_o + rh * p.head_dim + 4 * q;
-#pragma unroll 8
-  for (int c = 0; c < S; ++c) {
-    const float w = expf(p.part_lse[c * RH + rh] - M);  // 0 for an empty part (lse = -inf)
-    const f32x4 v = *reinterpret_cast<const f32x4 *>(o4 + c * RH * p.head_dim);
-    W += w;
-    if (w > 0.0f) {  // an empty part contributes nothing, whatever its o holds
-      acc[0] = fmaf(w, v[0], acc[0]);
-      acc[1] = fmaf(w, v[1], acc[1]);
-      acc[2] = fmaf(w, v[2], acc[2]);
-      acc[3] = fmaf(w, v[3], acc[3]);
-    }
   }
   const float inv = 1.0f / W;
 #pragma unroll
