@@ -1,0 +1,61 @@
+"""CPU oracle for top-k list construction (test infrastructure).
+
+Only the test suite, ``__graft_entry__.smoke()`` and the benchmark's
+``cpu_baseline`` leg may import this module; the product path never does.
+Plain Python on purpose: one query at a time, straight from the definitions.
+
+Source: DeepSeek-V4 CSA/HCA article, §2.3 (the list of a query is the
+concatenation of its sliding-window indices and its compressed-region
+indices) and §3.3 (cache layout ``[b, window + max_len / ratio, d]``: the
+window region is a ring in which position ``p`` is written to slot
+``p % window``; the compressor emits compressed token ``c`` once position
+``(c + 1) * ratio - 1`` has been seen, i.e. when ``(pos + 1) % ratio == 0``,
+and its row follows the window region).
+
+Readings (the article shows the pieces, not the builder):
+  * query position ``p`` sees the window positions ``max(0, p - window + 1)
+    .. p`` (the ring holds the last ``window`` positions, itself included),
+    listed by ring slot in increasing position order, then ``-1`` up to
+    ``window`` entries;
+  * it sees compressed token ``c`` iff ``(c + 1) * ratio - 1 <= p`` and
+    ``c < n_comp`` (the cache holds ``n_comp`` compressed rows), listed as row
+    ``window + c`` in increasing ``c``, then ``-1`` up to ``n_comp`` entries;
+  * ``ratio == 0`` means no compressed region (``n_comp`` must be 0);
+  * a negative position sees nothing.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def query_list(p: int, window: int, ratio: int, n_comp: int) -> list[int]:
+    """The ``window + n_comp`` list entries of one query at absolute position p."""
+    win = []
+    if p >= 0:
+        for q in range(max(0, p - window + 1), p + 1):
+            win.append(q % window)
+    win += [-1] * (window - len(win))
+    comp = []
+    if ratio > 0:
+        for c in range(n_comp):
+            if (c + 1) * ratio - 1 <= p:
+                comp.append(window + c)
+    comp += [-1] * (n_comp - len(comp))
+    return win + comp
+
+
+def topk_lists(start_pos, q_len: int, window: int, ratio: int, n_comp: int, rows=None) -> np.ndarray:
+    """Lists of queries (b, t) at positions start_pos[b] + t.
+
+    Returns int32 [B, q_len, window + n_comp], or [len(rows), window + n_comp] for the flat
+    query rows ``b * q_len + t`` named in ``rows``.
+    """
+    sp = np.asarray(start_pos, dtype=np.int64).reshape(-1)
+    B = sp.shape[0]
+    K = window + n_comp
+    flat = range(B * q_len) if rows is None else [int(r) for r in rows]
+    out = np.empty((len(flat), K), dtype=np.int32)
+    for i, r in enumerate(flat):
+        b, t = divmod(r, q_len)
+        out[i] = query_list(int(sp[b]) + t, window, ratio, n_comp)
+    return out.reshape(B, q_len, K) if rows is None else out
