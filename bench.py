@@ -63,6 +63,7 @@ def _traffic(workload: str):
 class Workload:
     name: str
     bound: str
+    unit = "pairs/s"  # attended (query, head, key) pairs; the list builder counts list entries
 
     def __init__(self, device):
         self.device = device
@@ -145,6 +146,33 @@ class IndexedWorkload(Workload):
                           workspace=self.workspace)
 
 
+class BuildIdxWorkload(Workload):
+    """Device-side top-k lists at the prefill shape: 8192 queries at positions 24576.., ring 128,
+    ratio 4, 8192 compressed rows -> [1, 8192, 8320] int32 (a pure store stream)."""
+
+    def __init__(self, device, name, start_pos, q_len, window, ratio, n_comp):
+        import torch
+        super().__init__(device)
+        self.name = name
+        self.bound = "hbm"
+        self.case0 = None
+        self.args = dict(window=window, ratio=ratio, n_comp=n_comp)
+        self.q_len = q_len
+        self.sp = torch.tensor(start_pos, dtype=torch.int32, device=device)
+        K = window + n_comp
+        self.out = [torch.empty((len(start_pos), q_len, K), dtype=torch.int32, device=device) for _ in range(2)]
+        self.bytes = len(start_pos) * q_len * K * 4 + len(start_pos) * 4
+        self.pairs = len(start_pos) * q_len * K  # list entries written
+        self.flops = 0
+        self.unit = "list entries/s"
+        self.config = dict(workload=name, batch=len(start_pos), q_len=q_len, window=window, ratio=ratio,
+                           n_comp=n_comp, start_pos=int(start_pos[0]))
+
+    def launch(self, i):
+        import sliding_window_attention_index_amd as sattn
+        sattn.build_topk_idxs(self.sp, self.q_len, out=self.out[i % 2], **self.args)
+
+
 def build_workload(name, device):
     import workloads as W
     if name == "vision_window":
@@ -158,6 +186,8 @@ def build_workload(name, device):
     if name == "sparse_decode":
         c = W.sparse_decode_case(seed=0, index_sets=16)
         return IndexedWorkload(device, name, c, c.extra["idx_sets"], q_sets=1, bound="hbm")
+    if name == "topk_idx_build":
+        return BuildIdxWorkload(device, name, [24576], 8192, 128, 4, 8192)
     raise ValueError(name)
 
 
@@ -273,7 +303,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="vision_window",
-                    choices=["vision_window", "causal_window_null", "sparse_prefill", "sparse_decode"])
+                    choices=["vision_window", "causal_window_null", "sparse_prefill", "sparse_decode",
+                             "topk_idx_build"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-extra", action="store_true", help="time only the headline workload")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -301,8 +332,8 @@ def main():
 
     names = [args.workload]
     if not args.no_extra:
-        names += [n for n in ("vision_window", "causal_window_null", "sparse_prefill", "sparse_decode")
-                  if n != args.workload]
+        names += [n for n in ("vision_window", "causal_window_null", "sparse_prefill", "sparse_decode",
+                              "topk_idx_build") if n != args.workload]
     results = {}
     main_wl = None
     for name in names:
@@ -311,7 +342,7 @@ def main():
         steps = args.steps
         wall, mean_ev, med_ev = time_workload(wl, steps, args.warmup)
         ms = wall / steps * 1e3
-        rec = {"value": round(wl.pairs / (ms / 1e3), 1), "unit": "pairs/s", "ms_per_step": round(ms, 5),
+        rec = {"value": round(wl.pairs / (ms / 1e3), 1), "unit": wl.unit, "ms_per_step": round(ms, 5),
                "kernel_ms_mean": round(mean_ev, 5), "kernel_ms_median": round(med_ev, 5), "pairs": wl.pairs,
                "config": wl.config, "roofline": roofline(wl, mean_ev)}
         print(f"[bench] {name}: {json.dumps(rec)}", file=sys.stderr, flush=True)
@@ -326,7 +357,7 @@ def main():
     line = {
         "metric": "attended q-k pairs/sec",
         "value": head["value"],
-        "unit": "pairs/s",
+        "unit": head["unit"],
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define SATTN_ABI_VERSION 1
+#define SATTN_ABI_VERSION 2
 
 typedef enum {
   SATTN_OK = 0,
@@ -191,6 +191,42 @@ typedef struct {
   void *o;
   float *lse;
 } sattn_merge_args;
+
+/*
+ * Top-k lists of the indexed path built on the device (DeepSeek-V4 CSA/HCA
+ * article: §2.3, a query's list is its sliding-window indices followed by its
+ * compressed-region indices; §3.3, the cache of a batch row is
+ * [window + n_comp, d] with position p's row in ring slot p % window and
+ * compressed row c at window + c, compressed token c existing once position
+ * (c + 1) * ratio - 1 has been seen).
+ *
+ *   out       [batch, q_len, window + n_comp] int32 (written), the idx argument
+ *             of sattn_indexed_fwd with topk = window + n_comp
+ *   start_pos [batch] int32 device array: query t of batch row b sits at
+ *             absolute position start_pos[b] + t (a negative position sees
+ *             nothing)
+ *   window    ring size (>= 1)
+ *   ratio     tokens per compressed row; 0 = no compressed region (n_comp
+ *             must then be 0)
+ *   n_comp    compressed rows held by the cache (>= 0)
+ *
+ * Entry k < window of a query at position p is the ring slot of position
+ * max(0, p - window + 1) + k when that position is <= p, else -1; entry
+ * window + c is row window + c when (c + 1) * ratio - 1 <= p, else -1.  So a
+ * list holds its valid rows first in each part, in increasing position, then
+ * -1 padding; all valid rows are distinct.
+ */
+typedef struct {
+  int32_t *out;
+  const int32_t *start_pos;
+  int32_t batch;
+  int32_t q_len;
+  int32_t window;
+  int32_t ratio;
+  int32_t n_comp;
+} sattn_build_idx_args;
+
+sattn_status sattn_build_topk_idxs(const sattn_build_idx_args *args, hipStream_t stream);
 
 sattn_status sattn_window_fwd(const sattn_window_args *args, hipStream_t stream);
 sattn_status sattn_indexed_fwd(const sattn_indexed_args *args, hipStream_t stream);

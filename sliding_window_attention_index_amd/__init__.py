@@ -9,6 +9,7 @@ built, importing works but every call raises.
                    sinks=sinks, sink_mode="key0")
     o = indexed_fwd(q, kv, topk_idxs, sinks=sinks, sink_mode="null", num_splits=8)
     o = merge_lse(part_o, part_lse, sinks=sinks, sink_mode="null")
+    idx = build_topk_idxs(start_pos, q_len, window=128, ratio=4, n_comp=8192)
 """
 from __future__ import annotations
 
@@ -18,8 +19,8 @@ import os
 
 import torch  # loads the HIP runtime libsattn links against
 
-__all__ = ["window_fwd", "indexed_fwd", "merge_lse", "indexed_workspace_size", "SattnError", "library_path",
-           "load_library", "abi_version", "SINK_MODES"]
+__all__ = ["window_fwd", "indexed_fwd", "merge_lse", "build_topk_idxs", "indexed_workspace_size", "SattnError",
+           "library_path", "load_library", "abi_version", "SINK_MODES"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_NAME = "libsattn.so"
@@ -59,6 +60,12 @@ class _MergeArgs(ctypes.Structure):
                 ("o", ctypes.c_void_p), ("lse", ctypes.c_void_p)]
 
 
+class _BuildIdxArgs(ctypes.Structure):
+    _fields_ = [("out", ctypes.c_void_p), ("start_pos", ctypes.c_void_p), ("batch", ctypes.c_int32),
+                ("q_len", ctypes.c_int32), ("window", ctypes.c_int32), ("ratio", ctypes.c_int32),
+                ("n_comp", ctypes.c_int32)]
+
+
 _LIB = None
 
 
@@ -79,6 +86,8 @@ def load_library(path: str | None = None):
     lib.sattn_indexed_fwd.restype = ctypes.c_int
     lib.sattn_merge_lse.argtypes = [ctypes.POINTER(_MergeArgs), P]
     lib.sattn_merge_lse.restype = ctypes.c_int
+    lib.sattn_build_topk_idxs.argtypes = [ctypes.POINTER(_BuildIdxArgs), P]
+    lib.sattn_build_topk_idxs.restype = ctypes.c_int
     lib.sattn_indexed_workspace_size.argtypes = [ctypes.c_int32] * 5
     lib.sattn_indexed_workspace_size.restype = ctypes.c_size_t
     lib.sattn_status_string.argtypes = [ctypes.c_int]
@@ -223,3 +232,26 @@ def merge_lse(part_o, part_lse, *, sinks=None, sink_mode="none", out_dtype=torch
     if st != 0:
         raise SattnError(st, "sattn_merge_lse")
     return (o, lse) if return_lse else o
+
+
+def build_topk_idxs(start_pos, q_len: int, *, window: int, ratio: int, n_comp: int, out=None):
+    """Top-k lists [batch, q_len, window + n_comp] int32 of queries at positions start_pos[b] + t.
+
+    Each list is the query's window ring slots, then its visible compressed rows (window + c),
+    -1 padded; the result is the `topk_idxs` of `indexed_fwd` over a cache [window + n_comp, d].
+    """
+    dev = start_pos.device
+    _check_dev("start_pos", start_pos, dev, torch.int32)
+    B = start_pos.shape[0]
+    K = window + n_comp
+    if out is None:
+        out = torch.empty((B, q_len, K), dtype=torch.int32, device=dev)
+    else:
+        _check_dev("out", out, dev, torch.int32)
+        if tuple(out.shape) != (B, q_len, K):
+            raise ValueError(f"out must have shape {(B, q_len, K)}")
+    a = _BuildIdxArgs(_ptr(out), _ptr(start_pos), B, q_len, window, ratio, n_comp)
+    st = _lib_handle().sattn_build_topk_idxs(ctypes.byref(a), _stream(dev))
+    if st != 0:
+        raise SattnError(st, "sattn_build_topk_idxs")
+    return out

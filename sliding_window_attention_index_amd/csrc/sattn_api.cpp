@@ -7,6 +7,8 @@
 // producer's event was waited on read unfinished data).
 #include "sattn.h"
 
+#include <cstdint>
+
 #include <math.h>
 #include <stdint.h>
 
@@ -106,6 +108,25 @@ sattn_status sattn_window_fwd(const sattn_window_args *a, hipStream_t stream) {
   if (a->dtype == SATTN_BF16 && sattn::window_mfma_supported(p))
     return launch_status(sattn::launch_window_mfma(p, stream));
   return launch_status(sattn::launch_window_valu(p, a->dtype == SATTN_F32 ? sattn::kF32 : sattn::kBF16, stream));
+}
+
+sattn_status sattn_build_topk_idxs(const sattn_build_idx_args *a, hipStream_t stream) {
+  if (!a) return SATTN_ERR_NULL_PTR;
+  if (a->batch < 0 || a->q_len < 0 || a->window < 1 || a->n_comp < 0) return SATTN_ERR_SHAPE;
+  if (a->ratio < 0 || (a->ratio == 0 && a->n_comp > 0)) return SATTN_ERR_ARG;
+  if (static_cast<int64_t>(a->window) + a->n_comp > INT32_MAX) return SATTN_ERR_SHAPE;
+  if (a->batch == 0 || a->q_len == 0) return SATTN_OK;
+  if (!a->out || !a->start_pos) return SATTN_ERR_NULL_PTR;
+  if (!aligned4(a->out) || !aligned4(a->start_pos)) return SATTN_ERR_ALIGNMENT;
+  sattn::BuildIdxParams p;
+  p.out = a->out;
+  p.start_pos = a->start_pos;
+  p.batch = a->batch;
+  p.q_len = a->q_len;
+  p.window = a->window;
+  p.ratio = a->ratio;
+  p.n_comp = a->n_comp;
+  return launch_status(sattn::launch_build_topk_idxs(p, stream));
 }
 
 sattn_status sattn_merge_lse(const sattn_merge_args *a, hipStream_t stream) {

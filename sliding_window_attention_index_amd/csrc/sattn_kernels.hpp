@@ -24,6 +24,13 @@ struct WindowParams {
   int sink_mode;
 };
 
+// Device-side top-k list construction.
+struct BuildIdxParams {
+  int32_t *out;              // [batch, q_len, window + n_comp]
+  const int32_t *start_pos;  // [batch]
+  int batch, q_len, window, ratio, n_comp;
+};
+
 // Indexed path: one shared K=V head per batch row, top-k lists.
 struct IndexedParams {
   const void *q;        // [B, M, H, D]
@@ -61,5 +68,7 @@ bool window_mfma_supported(const WindowParams &p);
 hipError_t launch_window_mfma(const WindowParams &p, hipStream_t stream);
 bool indexed_mfma_supported(const IndexedParams &p);
 hipError_t launch_indexed_mfma(const IndexedParams &p, hipStream_t stream);
+
+hipError_t launch_build_topk_idxs(const BuildIdxParams &p, hipStream_t stream);
 
 }  // namespace sattn

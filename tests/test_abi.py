@@ -11,7 +11,7 @@ import re
 import pytest
 
 import sliding_window_attention_index_amd as sattn
-from sliding_window_attention_index_amd import _IndexedArgs, _MergeArgs, _WindowArgs
+from sliding_window_attention_index_amd import _BuildIdxArgs, _IndexedArgs, _MergeArgs, _WindowArgs
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sattn.h")
@@ -35,7 +35,7 @@ def _declared_functions():
 
 def test_header_functions_exported(lib):
     names = _declared_functions()
-    assert set(names) == {"sattn_window_fwd", "sattn_indexed_fwd", "sattn_merge_lse",
+    assert set(names) == {"sattn_window_fwd", "sattn_indexed_fwd", "sattn_merge_lse", "sattn_build_topk_idxs",
                           "sattn_indexed_workspace_size", "sattn_status_string", "sattn_abi_version"}
     for name in names:
         assert hasattr(lib, name), name
@@ -150,3 +150,32 @@ def _merge(**kw):
 ])
 def test_merge_validation(lib, kw, status):
     assert lib.sattn_merge_lse(ctypes.byref(_merge(**kw)), None) == status
+
+
+def _build(**kw):
+    base = dict(out=FAKE, start_pos=FAKE, batch=64, q_len=1, window=128, ratio=4, n_comp=32768)
+    base.update(kw)
+    return _BuildIdxArgs(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(window=0), SHAPE),
+    (dict(batch=-1), SHAPE),
+    (dict(q_len=-2), SHAPE),
+    (dict(n_comp=-1), SHAPE),
+    (dict(ratio=-4), ARG),
+    (dict(ratio=0), ARG),                      # compressed rows without a ratio
+    (dict(window=2**31 - 10, n_comp=100), SHAPE),
+    (dict(out=None), NULL_PTR),
+    (dict(start_pos=None), NULL_PTR),
+    (dict(out=FAKE + 2), ALIGNMENT),
+    (dict(start_pos=FAKE + 1), ALIGNMENT),
+])
+def test_build_topk_idxs_validation(lib, kw, status):
+    assert lib.sattn_build_topk_idxs(ctypes.byref(_build(**kw)), None) == status
+
+
+def test_build_topk_idxs_empty_is_noop(lib):
+    assert lib.sattn_build_topk_idxs(ctypes.byref(_build(batch=0, out=None, start_pos=None)), None) == OK
+    assert lib.sattn_build_topk_idxs(ctypes.byref(_build(q_len=0, out=None)), None) == OK
+    assert lib.sattn_build_topk_idxs(None, None) == NULL_PTR
