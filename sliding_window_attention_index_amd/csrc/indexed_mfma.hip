@@ -7,27 +7,23 @@
 // dense GEMMs, then runs the online softmax over chunks and adds the
 // per-head null-logit sink to the denominator at the end.
 //
-// gfx950 mapping (one wave64 per task = one query, 32*HB of its heads, one
-// slice of its list):
-//   * S^T = KV . Q^T with v_mfma_f32_32x32x16_bf16.  The M dimension is 32
-//     gathered keys, N is 32 heads, K runs over head_dim.  Lane (n, h) loads
-//     head_dim/2 contiguous elements of key n's row straight from global
-//     memory into the A-operand registers (the contraction order over
-//     head_dim is permuted identically in A and B, so each lane reads one
-//     contiguous half-row: 16-byte loads, no LDS round trip for QK).
-//   * The accumulator layout of S^T puts 16 keys of one head in each lane and
-//     the other 16 in lane ^ 32, so the row max / row sum need one
-//     v_permlane32_swap instead of a 32-lane reduction.
-//   * The same registers are written to a per-wave LDS tile, and the PV
-//     product O^T = KV^T . P^T reads KV^T with ds_read_b64_tr_b16 (four keys
-//     of one dimension per lane).  P^T is the S^T accumulator converted to
-//     bf16 in place: the keys of MFMA step t are the accumulator registers
-//     8t..8t+7, and the transposed reads fetch exactly those keys.
-//   * The O^T accumulator holds one head per lane, so rescaling by the
-//     per-head factor is a per-lane multiply; it is skipped unless the
-//     running maximum grows by more than 2^8 (the stale maximum cancels in
-//     o = acc / l, and p <= 256 stays exact enough in bf16/fp32).
-//   * Gathers for block b+1 are issued before block b is computed.
+// gfx950 mapping (one wave64 per task = one query, 32 of its heads, one slice
+// of its list; the four waves of a workgroup are independent):
+//   * The slice's list entries are staged in a wave-private LDS area; the
+//     wave then streams its 32-row blocks into a private ring of NT swizzled
+//     LDS tiles with buffer_load ... lds (each instruction fetches four whole
+//     rows; a row that is not listed is read out of bounds and lands as
+//     zeros).  NT blocks are in flight at once and no register holds a row
+//     in transit; the wave waits for its own DMAs only (vmcnt), no barrier.
+//   * S^T = K . Q^T with v_mfma_f32_32x32x16_bf16: A = 16-byte reads of the
+//     tile rows (keys), B = the 32 heads' q in registers; the accumulator
+//     holds 16 keys of one head per lane and the other 16 in lane ^ 32.
+//   * O^T += V^T . P^T: the same tile read with ds_read_b64_tr_b16 (the cache
+//     row is the value too), P^T = the S^T accumulator rounded to bf16.
+//   * Online softmax with a lazy rescale (only when the running maximum grows
+//     by more than 2^8); the output goes through LDS so that it is written as
+//     whole rows (the 32 heads of a query are one contiguous stretch).
+#include "lds_tile.hpp"
 #include "sattn_device.hpp"
 #include "sattn_kernels.hpp"
 #include "softmax_block.hpp"
@@ -36,7 +32,7 @@ namespace sattn {
 namespace {
 
 constexpr int kBlockKeys = 32;
-constexpr int kPad = 16;  // LDS row padding (bf16 elements): keeps the transposed reads conflict-free
+constexpr int kIdxCap = 1024;  // list entries staged per wave at a time
 
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -44,27 +40,28 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_list_rsrc(const int32_t *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t *>(base), static_cast<short>(0),
-                                           static_cast<int>(bytes), 0x00020000);
+// LDS read of one dword the compiler does not see (it would otherwise wait for every DMA in
+// flight before reading LDS); the result is tied to an lgkmcnt(0) wait.
+__device__ __forceinline__ int ds_read_i32(uint32_t addr) {
+  int r;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(r) : "v"(addr));
+  return r;
 }
 
-__device__ __forceinline__ bf16x4 lds_read_tr(const __bf16 *p) {
-  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p));
-}
-
-template <int D>
+template <int D, int NT>
 __global__ __launch_bounds__(256) void indexed_fwd_mfma(IndexedParams p) {
-  constexpr int S = D / 16;   // MFMA steps over head_dim
-  constexpr int DB = D / 32;  // 32-wide blocks of output dims
-  constexpr int LDSS = D + kPad;
-  __shared__ __attribute__((aligned(16))) __bf16 tiles[4][kBlockKeys * LDSS];
+  using Tile = SwizzledTile<D>;
+  constexpr int S = D / 16;                  // MFMA steps over head_dim
+  constexpr int DB = D / 32;                 // 32-wide blocks of output dims
+  constexpr int kDpb = Tile::kDmaPerTile;    // DMA instructions per 32-row block
+  static_assert((NT & (NT - 1)) == 0 && NT >= 2 && NT <= 4, "ring size");
+  __shared__ __attribute__((aligned(1024))) char tiles[4][NT * Tile::kBytes];
+  __shared__ __attribute__((aligned(16))) int32_t lists[4][kIdxCap];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = lane_id();
   const int h = lane >> 5;   // half of the wave: which half of head_dim / which key quads
-  const int n = lane & 31;   // key row (A operand) / head column (B operand and outputs)
+  const int n = lane & 31;   // key row (A operand) / head (B operand and outputs)
   const int H = p.num_heads, N = p.kv_len, K = p.topk;
   const int n_hg = H / 32;
   const int64_t BM = static_cast<int64_t>(p.batch) * p.q_len;
@@ -80,7 +77,7 @@ __global__ __launch_bounds__(256) void indexed_fwd_mfma(IndexedParams p) {
   const bool key0 = p.sink_mode == kSinkKey0;
   const bool null_sink = !partial && p.sink_mode == kSinkNull;
 
-  // B operand of S^T: q[bt, head0 + n, h*D/2 + 8s .. +8].
+  // B operand of S^T: q[bt, head0 + n, h*D/2 + 8s .. +8] (logical chunk h*S + s of the row).
   bf16x8 qf[S];
   {
     const __bf16 *qrow = static_cast<const __bf16 *>(p.q) + (bt * H + head0 + n) * D + h * (D / 2);
@@ -99,50 +96,66 @@ __global__ __launch_bounds__(256) void indexed_fwd_mfma(IndexedParams p) {
 
   const int kb = part * p.part_len;
   const int ke = min(K, kb + p.part_len);
-  const int nblk = (max(0, ke - kb) + kBlockKeys - 1) / kBlockKeys;
-  // List entries through a bounds-checked buffer resource (reads past the list return 0; entries
-  // past the slice are turned into -1 explicitly).
-  const __amdgpu_buffer_rsrc_t lrs = make_list_rsrc(p.idx + bt * K, static_cast<uint32_t>(K) * 4u);
-  // This batch row's cache through a buffer resource: a lane without a row reads past its end
-  // and gets zeros.
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<void *>(static_cast<const void *>(static_cast<const __bf16 *>(p.kv) + b * static_cast<int64_t>(N) * D)),
-      static_cast<short>(0), static_cast<int>(static_cast<uint32_t>(N) * D * 2u), 0x00020000);
-  __bf16 *tile = tiles[wave];
+  // This batch row's cache and this query's list through bounds-checked buffer resources.
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(static_cast<const __bf16 *>(p.kv) + b * static_cast<int64_t>(N) * D,
+                                               static_cast<uint32_t>(N) * D * 2u);
+  const __amdgpu_buffer_rsrc_t lrs = make_rsrc(p.idx + bt * K, static_cast<uint32_t>(K) * 4u);
+  char *ring = tiles[wave];
+  const uint32_t ring_addr = lds_addr(ring);
+  int32_t *list = lists[wave];
+  const uint32_t list_addr = lds_addr(list);
 
-  // Index of this lane's row in block blk (-1: none).
-  auto load_idx = [&](int blk) -> int {
-    const int slot = kb + blk * kBlockKeys + n;
-    const int x = __builtin_amdgcn_raw_buffer_load_b32(lrs, static_cast<uint32_t>(slot) * 4u, 0, 0);
-    return slot < ke ? x : -1;
-  };
-  // Gather the lane's half row of block blk's row x (zero if x is not a row).
-  struct Gathered {
-    bf16x8 v[S];
-    uint32_t vmask, zmask;  // rows that exist; rows that are cache row 0
-  };
-  auto gather = [&](int x, Gathered &g) {
-    const bool valid = x >= 0 && x < N;
-    g.vmask = static_cast<uint32_t>(__ballot(valid));
-    g.zmask = key0 ? static_cast<uint32_t>(__ballot(valid && x == 0)) : 0u;
-    const uint32_t off = valid ? static_cast<uint32_t>(x) * (D * 2u) + h * D : 0xfffff000u;
+  // DMA instruction u of a block fills the tile's bytes [1024 u, 1024 (u + 1)): lane l fetches the
+  // swizzled chunk of one of its rows (Tile::dma_source).
+  auto issue_block = [&](int j) {  // block j of the staged chunk into ring slot j % NT
+    char *dst = ring + (j & (NT - 1)) * Tile::kBytes;
 #pragma unroll
-    for (int s = 0; s < S; ++s)
-      g.v[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, off + s * 16u, 0, 0));
+    for (int u = 0; u < kDpb; ++u) {
+      int row, chunk;
+      Tile::dma_source(u, lane, row, chunk);
+      const int x = ds_read_i32(list_addr + (j * kBlockKeys + row) * 4);
+      const bool valid = x >= 0 && x < N;
+      const uint32_t off = valid ? static_cast<uint32_t>(x) * Tile::kRowBytes + chunk * 16 : 0xfffff000u;
+      dma16(krs, dst + u * 1024, off);
+    }
   };
 
-  const int g16 = lane >> 4, i16 = lane & 15;
-  auto compute = [&](const Gathered &g) {
-    if (g.vmask == 0u) return;
-    wave_lds_sync();  // the previous block's transposed reads are done
+  // LDS operand addresses (bits 4..7 of every tile base are clear, see the window kernel):
+  // K rows: row n, logical chunk h*S + s at kbase ^ 16 s; V^T quads at vbase ^ (64 db + 16 e) plus
+  // rows 8 e + 16 tt.
+  const uint32_t kbase = ring_addr + Tile::offset(n, h * S);
+  uint32_t vbase;
+  {
+    const int g16 = lane >> 4, i16 = lane & 15;
+    const int c2 = 2 * (g16 & 1) + ((i16 & 3) >> 1);
+    vbase = ring_addr + Tile::offset(4 * h + (i16 >> 2), c2) + (i16 & 1) * 8;
+  }
+  constexpr int kRow8 = 8 * Tile::kRowBytes;
+
+  auto compute = [&](int slot, uint32_t vmask, uint32_t zmask) {
+    uint32_t kb_ = kbase + slot * Tile::kBytes;  // opaque per block: the XORed addresses stay local
+    asm volatile("" : "+v"(kb_));
+    u32x4 kf[S];
 #pragma unroll
-    for (int s = 0; s < S; ++s) *reinterpret_cast<bf16x8 *>(tile + n * LDSS + h * (D / 2) + s * 8) = g.v[s];
+    for (int s = 0; s < S; ++s) kf[s] = ds_read_b128<0>(kb_ ^ (16u * s));
+    lgkm_fence<0>(kf);
     f32x16 st = f32x16{};
 #pragma unroll
-    for (int s = 0; s < S; ++s) st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(g.v[s], qf[s], st, 0, 0, 0);
+    for (int s = 0; s < S; ++s)
+      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[s]), qf[s], st, 0, 0, 0);
+    uint32_t vb = vbase + slot * Tile::kBytes;
+    asm volatile("" : "+v"(vb));
+    u32x2 vr[4 * DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      vr[db * 2] = ds_read_tr_b16<0>(vb ^ (64u * db));
+      vr[db * 2 + 1] = ds_read_tr_b16<kRow8>(vb ^ (64u * db + 16u));
+      vr[2 * DB + db * 2] = ds_read_tr_b16<2 * kRow8>(vb ^ (64u * db));
+      vr[2 * DB + db * 2 + 1] = ds_read_tr_b16<3 * kRow8>(vb ^ (64u * db + 16u));
+    }
     // Accumulator element r of lane (n, h) is key 8*(r/4) + 4h + r%4 of head n.
-    if (g.zmask) bias_block(st, g.zmask, h, sink_raw);
-    if (g.vmask != 0xffffffffu) mask_block(st, g.vmask, h);
+    if (zmask) bias_block(st, zmask, h, sink_raw);
+    if (vmask != 0xffffffffu) mask_block(st, vmask, h);
     float alpha;
     if (softmax_need_rescale(rs, block_max(st), c, alpha)) {
 #pragma unroll
@@ -150,84 +163,98 @@ __global__ __launch_bounds__(256) void indexed_fwd_mfma(IndexedParams p) {
     }
     bf16x8 pb[2];
     softmax_probs(st, rs, c, pb);
-    wave_lds_sync();  // the rows written above are visible to the whole wave
-    // O^T[d][head] += KV^T[d][keys] . P^T[keys][head]; step tt covers keys 16tt..16tt+15 with
-    // lane half h holding keys 16tt+4h+{0..3} and 16tt+8+4h+{0..3}.
+    lgkm_fence<0>(vr);
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int ka = 16 * tt + 4 * h + (i16 >> 2);
+    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const int col = 32 * db + 16 * (g16 & 1) + (i16 & 3) * 4;
-        const bf16x4 ra = lds_read_tr(tile + ka * LDSS + col);
-        const bf16x4 rb = lds_read_tr(tile + (ka + 8) * LDSS + col);
-        const bf16x8 a = {ra[0], ra[1], ra[2], ra[3], rb[0], rb[1], rb[2], rb[3]};
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[tt], acc[db], 0, 0, 0);
+        const u32x2 ra = vr[(tt * DB + db) * 2], rb = vr[(tt * DB + db) * 2 + 1];
+        const u32x4 av = {ra[0], ra[1], rb[0], rb[1]};
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pb[tt], acc[db], 0, 0, 0);
       }
-    }
   };
 
-  // Pipeline: the indices of blocks b+1..b+4 are in flight or held in a 4-entry ring, the rows of
-  // block b+1 are gathered while block b is computed (two row buffers used in turn).
-  int ix[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) ix[j] = load_idx(j);
-  Gathered ga, gb;
-  if (nblk > 0) gather(ix[0], ga);
-  ix[0] = load_idx(4);
-  auto step = [&](int blk, const Gathered &cur, Gathered &nxt, int &ixs) {
-    if (blk + 1 < nblk) {
-      gather(ixs, nxt);  // block blk + 1
-      ixs = load_idx(blk + 5);
+  for (int c0 = kb; c0 < ke; c0 += kIdxCap) {
+    const int cend = min(ke, c0 + kIdxCap);
+    const int nblk = (cend - c0 + kBlockKeys - 1) / kBlockKeys;
+    asm volatile("" ::: "memory");  // the previous chunk's list reads (inline asm) stay before these stores
+    // Stage the chunk's entries (-1 past its end).  Every DMA of the previous chunk has been
+    // waited for, so nothing reads or fills LDS meanwhile.
+    for (int j = lane; j < nblk * kBlockKeys; j += 64) {
+      const int e = c0 + j;
+      const int x = __builtin_amdgcn_raw_buffer_load_b32(lrs, static_cast<uint32_t>(e) * 4u, 0, 0);
+      list[j] = e < cend ? x : -1;
     }
-    compute(cur);
-  };
-  for (int b0 = 0; b0 < nblk; b0 += 4) {
-    step(b0, ga, gb, ix[1]);
-    if (b0 + 1 < nblk) step(b0 + 1, gb, ga, ix[2]);
-    if (b0 + 2 < nblk) step(b0 + 2, ga, gb, ix[3]);
-    if (b0 + 3 < nblk) step(b0 + 3, gb, ga, ix[0]);
+    wave_lds_sync();
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+      if (j < nblk) issue_block(j);
+    for (int j = 0; j < nblk; ++j) {
+      // This wave's DMAs younger than block j's: those of the next min(NT - 1, nblk - 1 - j) blocks.
+      const int younger = min(NT - 1, nblk - 1 - j);
+      if (younger == 3) wait_vmcnt<3 * kDpb>();
+      else if (younger == 2) wait_vmcnt<2 * kDpb>();
+      else if (younger == 1) wait_vmcnt<kDpb>();
+      else wait_vmcnt<0>();
+      const int x = ds_read_i32(list_addr + (j * kBlockKeys + n) * 4);
+      const bool valid = x >= 0 && x < N;
+      const uint32_t vmask = static_cast<uint32_t>(__ballot(valid));
+      const uint32_t zmask = key0 ? static_cast<uint32_t>(__ballot(valid && x == 0)) : 0u;
+      if (vmask != 0u) compute(j & (NT - 1), vmask, zmask);
+      if (j + NT < nblk) issue_block(j + NT);  // the slot's reads are done (lgkm fences in compute)
+    }
   }
 
-  // Epilogue: o = acc / l, lse = ln(2) * (m + log2 l).  Lane (n, h) holds dims 32db + 8i + 4h + {0..3}.
-  const int head = head0 + n;
+  // Epilogue: o = acc / l, lse = ln(2) * (m + log2 l).  Lane (n, h) holds dims 32db + 8j + 4h + {0..3}
+  // of head n.  Each 32-dim block goes through the wave's first tile as scaled fp32 (16-byte chunk
+  // q of row r at q ^ (r & 7)) and comes back as 8 consecutive dims per lane.
   const float l_tot = halves_sum(rs.l);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   const float lse_v = l_tot > 0.0f ? (rs.m * c + log2f(l_tot)) * kLn2 : kNegInf;
-  if (partial) {
-    const int64_t row = (static_cast<int64_t>(part) * BM + bt) * H + head;
-    float *dst = p.part_o + row * D + 4 * h;
+  const int64_t row0 = partial ? (static_cast<int64_t>(part) * BM + bt) * H + head0 : bt * H + head0;
+  const int rl = lane >> 2, q4 = lane & 3;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+  for (int db = 0; db < DB; ++db) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f32x4 v = {acc[db][4 * i] * inv, acc[db][4 * i + 1] * inv, acc[db][4 * i + 2] * inv,
-                         acc[db][4 * i + 3] * inv};
-        *reinterpret_cast<f32x4 *>(dst + 32 * db + 8 * i) = v;
+    for (int j = 0; j < 4; ++j) {
+      const u32x4 w = {__float_as_uint(acc[db][4 * j] * inv), __float_as_uint(acc[db][4 * j + 1] * inv),
+                       __float_as_uint(acc[db][4 * j + 2] * inv), __float_as_uint(acc[db][4 * j + 3] * inv)};
+      ds_write_b128<0>(ring_addr + n * 128 + (((2 * j + h) ^ (n & 7)) << 4), w);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = 16 * i + rl;  // head head0 + r
+      u32x4 x[2];
+      x[0] = ds_read_b128<0>(ring_addr + r * 128 + (((2 * q4) ^ (r & 7)) << 4));
+      x[1] = ds_read_b128<0>(ring_addr + r * 128 + (((2 * q4 + 1) ^ (r & 7)) << 4));
+      lgkm_fence<0>(x);
+      const int64_t e0 = (row0 + r) * D + 32 * db + 8 * q4;
+      if (partial) {
+        *reinterpret_cast<u32x4 *>(p.part_o + e0) = x[0];
+        *reinterpret_cast<u32x4 *>(p.part_o + e0 + 4) = x[1];
+      } else {
+        const bf16x8 v = {static_cast<__bf16>(__uint_as_float(x[0][0])), static_cast<__bf16>(__uint_as_float(x[0][1])),
+                          static_cast<__bf16>(__uint_as_float(x[0][2])), static_cast<__bf16>(__uint_as_float(x[0][3])),
+                          static_cast<__bf16>(__uint_as_float(x[1][0])), static_cast<__bf16>(__uint_as_float(x[1][1])),
+                          static_cast<__bf16>(__uint_as_float(x[1][2])), static_cast<__bf16>(__uint_as_float(x[1][3]))};
+        *reinterpret_cast<bf16x8 *>(static_cast<__bf16 *>(p.o) + e0) = v;
       }
-    if (h == 0) p.part_lse[row] = lse_v;
-  } else {
-    __bf16 *dst = static_cast<__bf16 *>(p.o) + (bt * H + head) * D + 4 * h;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bf16x4 v = {static_cast<__bf16>(acc[db][4 * i] * inv), static_cast<__bf16>(acc[db][4 * i + 1] * inv),
-                          static_cast<__bf16>(acc[db][4 * i + 2] * inv),
-                          static_cast<__bf16>(acc[db][4 * i + 3] * inv)};
-        *reinterpret_cast<bf16x4 *>(dst + 32 * db + 8 * i) = v;
-      }
-    if (p.lse && h == 0) p.lse[bt * H + head] = lse_v;
+    }
+  }
+  if (h == 0) {
+    if (partial) p.part_lse[row0 + n] = lse_v;
+    else if (p.lse) p.lse[row0 + n] = lse_v;
   }
 }
 
-template <int D>
+template <int D, int NT>
 hipError_t launch(const IndexedParams &p, hipStream_t stream) {
   const int n_hg = p.num_heads / 32;
   const int64_t tasks = static_cast<int64_t>(p.batch) * p.q_len * n_hg * p.num_parts;
   const int64_t blocks = (tasks + 3) / 4;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((indexed_fwd_mfma<D>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((indexed_fwd_mfma<D, NT>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -241,7 +268,11 @@ bool indexed_mfma_supported(const IndexedParams &p) {
 }
 
 hipError_t launch_indexed_mfma(const IndexedParams &p, hipStream_t stream) {
-  return p.head_dim == 128 ? launch<128>(p, stream) : launch<64>(p, stream);
+  // Few tasks (decode-like): one workgroup per CU anyway, so each wave keeps four blocks in flight.
+  const int64_t tasks = static_cast<int64_t>(p.batch) * p.q_len * (p.num_heads / 32) * p.num_parts;
+  const bool deep = tasks < 4096;
+  if (p.head_dim == 128) return deep ? launch<128, 4>(p, stream) : launch<128, 2>(p, stream);
+  return deep ? launch<64, 4>(p, stream) : launch<64, 2>(p, stream);
 }
 
 }  // namespace sattn
