@@ -105,15 +105,27 @@ __global__ __launch_bounds__(256) void indexed_fwd_mfma(IndexedParams p) {
   int32_t *list = lists[wave];
   const uint32_t list_addr = lds_addr(list);
 
-  // DMA instruction u of a block fills the tile's bytes [1024 u, 1024 (u + 1)): lane l fetches the
-  // swizzled chunk of one of its rows (Tile::dma_source).
+  // DMA instruction u of a block fills the tile's bytes [1024 u, 1024 (u + 1)), i.e. tile rows
+  // u R .. u R + R - 1 (R = 1024 / row bytes); lane l serves row u R + g, g = l / (row bytes / 16),
+  // and fetches its swizzled chunk (Tile::dma_source).  Tile row u R + g holds list entry g U + u
+  // of the block (U = DMA instructions per block): any assignment of entries to rows gives the same
+  // attention, and this one gives each lane U consecutive entries, read with 16-byte LDS loads.
+  constexpr int kR = 1024 / Tile::kRowBytes;  // rows per DMA instruction
+  constexpr int kU = kDpb;                    // DMA instructions per block (kR * kU == 32)
+  static_assert(kR * kU == kBlockKeys && kU % 4 == 0, "block geometry");
+  const int dg = lane / (Tile::kRowBytes / 16);
+  auto entry_of_row = [](int r) { return (r % kR) * kU + r / kR; };
   auto issue_block = [&](int j) {  // block j of the staged chunk into ring slot j % NT
     char *dst = ring + (j & (NT - 1)) * Tile::kBytes;
+    u32x4 e4[kU / 4];
 #pragma unroll
-    for (int u = 0; u < kDpb; ++u) {
+    for (int v = 0; v < kU / 4; ++v) e4[v] = ds_read_b128<0>(list_addr + (j * kBlockKeys + dg * kU + 4 * v) * 4);
+    lgkm_fence<0>(e4);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
       int row, chunk;
-      Tile::dma_source(u, lane, row, chunk);
-      const int x = ds_read_i32(list_addr + (j * kBlockKeys + row) * 4);
+      Tile::dma_source(u, lane, row, chunk);  // row == u * kR + dg
+      const int x = static_cast<int>(e4[u / 4][u % 4]);
       const bool valid = x >= 0 && x < N;
       const uint32_t off = valid ? static_cast<uint32_t>(x) * Tile::kRowBytes + chunk * 16 : 0xfffff000u;
       dma16(krs, dst + u * 1024, off);
@@ -180,10 +192,26 @@ __global__ __launch_bounds__(256) void indexed_fwd_mfma(IndexedParams p) {
     asm volatile("" ::: "memory");  // the previous chunk's list reads (inline asm) stay before these stores
     // Stage the chunk's entries (-1 past its end).  Every DMA of the previous chunk has been
     // waited for, so nothing reads or fills LDS meanwhile.
-    for (int j = lane; j < nblk * kBlockKeys; j += 64) {
-      const int e = c0 + j;
-      const int x = __builtin_amdgcn_raw_buffer_load_b32(lrs, static_cast<uint32_t>(e) * 4u, 0, 0);
-      list[j] = e < cend ? x : -1;
+    {
+      // 16 bytes per lane per load, every load issued before any is used.
+      constexpr int kLoads = kIdxCap / 256;
+      u32x4 v[kLoads];
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i)
+        v[i] = (256 * i < nblk * kBlockKeys)
+                   ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   lrs, static_cast<uint32_t>(c0 + 256 * i + 4 * lane) * 4u, 0, 0))
+                   : u32x4{};
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) {
+        const int j = 256 * i + 4 * lane;
+        if (j < nblk * kBlockKeys) {
+          u32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = c0 + j + e < cend ? v[i][e] : 0xffffffffu;
+          *reinterpret_cast<u32x4 *>(list + j) = w;
+        }
+      }
     }
     wave_lds_sync();
     asm volatile("" ::: "memory");
@@ -197,7 +225,7 @@ __global__ __launch_bounds__(256) void indexed_fwd_mfma(IndexedParams p) {
       else if (younger == 2) wait_vmcnt<2 * kDpb>();
       else if (younger == 1) wait_vmcnt<kDpb>();
       else wait_vmcnt<0>();
-      const int x = ds_read_i32(list_addr + (j * kBlockKeys + n) * 4);
+      const int x = ds_read_i32(list_addr + (j * kBlockKeys + entry_of_row(n)) * 4);  // tile row n's entry
       const bool valid = x >= 0 && x < N;
       const uint32_t vmask = static_cast<uint32_t>(__ballot(valid));
       const uint32_t zmask = key0 ? static_cast<uint32_t>(__ballot(valid && x == 0)) : 0u;
