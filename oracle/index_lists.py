@@ -1,4 +1,4 @@
-"""CPU oracle for top-k list construction (test infrastructure).
+"""CPU oracle for top-k list construction and per-block attention mass (test infrastructure).
 
 Only the test suite, ``__graft_entry__.smoke()`` and the benchmark's
 ``cpu_baseline`` leg may import this module; the product path never does.
@@ -59,3 +59,41 @@ def topk_lists(start_pos, q_len: int, window: int, ratio: int, n_comp: int, rows
         b, t = divmod(r, q_len)
         out[i] = query_list(int(sp[b]) + t, window, ratio, n_comp)
     return out.reshape(B, q_len, K) if rows is None else out
+
+
+def block_mass(q, kv, topk_idxs, lse, *, scale: float, block_keys: int, sinks=None, sink_mode: int = 0,
+               rows=None) -> np.ndarray:
+    """Attention mass per block of list entries, normalised by a given log-sum-exp.
+
+    Source: nano-vllm "XAttention Offload Stream Synchronization Fix", technical details: the
+    third stage of the chunked estimate normalises with the global softmax statistics and sums
+    per block.  Reading: block c of a query's list is entries [c * block_keys, (c + 1) *
+    block_keys); its mass for head h is sum over its valid entries (0 <= idx < N) of
+    exp(scale * q[h] . kv[idx] + key-0 bias - lse[h]) with the key-0 sink bias of the
+    DeepSeek-V4 article's list convention (cache row 0).  With the lse of the same key set
+    (null sink included) the masses plus exp(sink - lse) sum to 1.
+
+    q [B, M, H, D], kv [B, N, D], topk_idxs [B, M, K], lse [B, M, H] (natural log).
+    Returns float64 [B*M or len(rows), H, ceil(K / block_keys)].
+    """
+    qf = np.asarray(q, dtype=np.float64) if not hasattr(q, "float") else q.float().numpy().astype(np.float64)
+    kvf = np.asarray(kv, dtype=np.float64) if not hasattr(kv, "float") else kv.float().numpy().astype(np.float64)
+    idx = np.asarray(topk_idxs)
+    ls = np.asarray(lse, dtype=np.float64)
+    B, M, H, D = qf.shape
+    N, K = kvf.shape[1], idx.shape[2]
+    nb = (K + block_keys - 1) // block_keys
+    snk = None if sinks is None else np.asarray(sinks, dtype=np.float64)
+    flat = range(B * M) if rows is None else [int(r) for r in rows]
+    out = np.zeros((len(flat), H, nb), dtype=np.float64)
+    for i, r in enumerate(flat):
+        b, t = divmod(r, M)
+        for k in range(K):
+            x = int(idx[b, t, k])
+            if x < 0 or x >= N:
+                continue
+            logit = scale * (qf[b, t] @ kvf[b, x])  # [H]
+            if sink_mode == 1 and x == 0:
+                logit = logit + snk
+            out[i, :, k // block_keys] += np.exp(logit - ls[b, t])
+    return out

@@ -8,15 +8,25 @@
 * The article's example (§2.2): a window list such as [100, 101, 102, 103].
 * Counts: min(p + 1, window) window rows and min(n_comp, (p + 1) // ratio) compressed rows.
 * Planted mistakes in a copy of the oracle must fail the simulation pin.
+
+Block mass (per-block attention mass normalised by the global log-sum-exp):
+* with the lse of the same key set, the masses plus the null sink's share sum to 1;
+* they equal a dense softmax over every cache row (unlisted rows masked, the null sink an
+  extra column) summed per block of list positions;
+* an lse merged from per-chunk partials normalises exactly as the one-pass lse;
+* planted mistakes (binning by cache row, dropped key-0 bias, unscaled logits) fail.
 """
 from __future__ import annotations
 
 import inspect
+import math
 import textwrap
 
 import numpy as np
 import pytest
+import torch
 
+import oracle
 from oracle import index_lists as IL
 
 
@@ -99,3 +109,108 @@ def test_planted_mistakes_fail(name):
     with pytest.raises(AssertionError):
         for window, ratio, n_comp, p_max in CASES:
             check_against_simulation(ns["query_list"], window, ratio, n_comp, p_max)
+
+
+# ---------------------------------------------------------------------------------------------
+# block mass (third stage of the chunked estimate: normalise with global statistics, sum per block)
+# ---------------------------------------------------------------------------------------------
+def _mass_inputs(seed, B=2, M=3, H=4, D=16, N=40, K=48, pad=True):
+    g = torch.Generator().manual_seed(seed)
+    rng = np.random.default_rng(seed)
+    q = torch.randn(B, M, H, D, generator=g)
+    kv = torch.randn(B, N, D, generator=g)
+    idx = np.full((B, M, K), -1, np.int32)
+    for b in range(B):
+        for t in range(M):
+            n = K - 9 if pad and t == 1 else min(K, N)
+            row = rng.choice(N, size=n, replace=False)
+            if t == 0 and 0 not in row:
+                row[0] = 0
+            idx[b, t, :n] = row
+    sinks = torch.randn(H, generator=g)
+    return q, kv, idx, sinks
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_block_mass_sums_to_one(mode):
+    q, kv, idx, sinks = _mass_inputs(1)
+    _, lse = oracle.indexed(q, kv, idx, scale=0.25, sinks=sinks, sink_mode=mode)
+    B, M, H = q.shape[:3]
+    mass = IL.block_mass(q, kv, idx, lse.reshape(B, M, H), scale=0.25, block_keys=8, sinks=sinks, sink_mode=mode)
+    total = mass.sum(-1)
+    if mode == 2:
+        total = total + np.exp(sinks.double().numpy()[None, :] - lse)
+    assert np.allclose(total, 1.0, atol=1e-12)
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_block_mass_matches_dense_softmax(mode):
+    """Dense softmax over all N cache rows (unlisted rows masked; null sink = extra column), then
+    the probability of each list entry's row summed per block of list positions."""
+    q, kv, idx, sinks = _mass_inputs(2)
+    B, M, H, D = q.shape
+    N, K = kv.shape[1], idx.shape[2]
+    _, lse = oracle.indexed(q, kv, idx, scale=0.25, sinks=sinks, sink_mode=mode)
+    mass = IL.block_mass(q, kv, idx, lse.reshape(B, M, H), scale=0.25, block_keys=16, sinks=sinks, sink_mode=mode)
+    for b in range(B):
+        for t in range(M):
+            logits = 0.25 * (q[b, t].double() @ kv[b].double().T)  # [H, N]
+            listed = torch.zeros(N, dtype=torch.bool)
+            for x in idx[b, t]:
+                if 0 <= x < N:
+                    listed[x] = True
+            logits = logits.masked_fill(~listed, -math.inf)
+            if mode == 1:
+                logits[:, 0] += sinks.double()
+            if mode == 2:
+                logits = torch.cat([logits, sinks.double()[:, None]], 1)
+            prob = torch.softmax(logits, -1)[:, :N]
+            want = np.zeros((H, (K + 15) // 16))
+            for k, x in enumerate(idx[b, t]):
+                if 0 <= x < N:
+                    want[:, k // 16] += prob[:, x].numpy()
+            assert np.allclose(mass[b * M + t], want, atol=1e-12)
+
+
+def test_block_mass_with_merged_statistics():
+    """The page's two stages before it: per-chunk statistics merged into global ones give the same
+    normalisation as one pass (stage 3 only needs the merged lse)."""
+    q, kv, idx, sinks = _mass_inputs(3)
+    B, M, H = q.shape[:3]
+    K = idx.shape[2]
+    _, lse1 = oracle.indexed(q, kv, idx, scale=0.25, sinks=sinks, sink_mode=2)
+    parts_o, parts_l = [], []
+    for c0 in range(0, K, 20):
+        sub = np.full_like(idx, -1)
+        sub[:, :, c0:c0 + 20] = idx[:, :, c0:c0 + 20]
+        o, l = oracle.indexed(q, kv, sub, scale=0.25)
+        parts_o.append(o)
+        parts_l.append(l)
+    _, lse2 = oracle.merge(np.stack(parts_o), np.stack(parts_l), sinks=sinks, sink_mode=2)
+    m1 = IL.block_mass(q, kv, idx, lse1.reshape(B, M, H), scale=0.25, block_keys=8, sinks=sinks, sink_mode=2)
+    m2 = IL.block_mass(q, kv, idx, lse2.reshape(B, M, H), scale=0.25, block_keys=8, sinks=sinks, sink_mode=2)
+    assert np.allclose(m1, m2, atol=1e-12)
+
+
+MASS_MUTANTS = {
+    "bins_by_cache_row": ("out[i, :, k // block_keys]", "out[i, :, min(x, K - 1) // block_keys]"),
+    "key0_bias_dropped": ("logit = logit + snk", "logit = logit"),
+    "unscaled_logit": ("logit = scale * (qf[b, t] @ kvf[b, x])", "logit = (qf[b, t] @ kvf[b, x])"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MASS_MUTANTS))
+def test_block_mass_planted_mistakes_fail(name):
+    old, new = MASS_MUTANTS[name]
+    src = textwrap.dedent(inspect.getsource(IL.block_mass))
+    assert old in src
+    ns = {"np": np}
+    exec(src.replace(old, new), ns)
+    saved = IL.block_mass
+    IL.block_mass = ns["block_mass"]
+    try:
+        with pytest.raises(AssertionError):
+            for mode in (1, 2):
+                test_block_mass_matches_dense_softmax(mode)
+    finally:
+        IL.block_mass = saved
