@@ -7,8 +7,9 @@ already resident in HBM.  The headline workload is the vision-encoder window
 attention (16 sequences, lengths U[1024, 4096], 16 query / 8 KV heads,
 head_dim 128, symmetric window 128, key-0 sinks, bf16).  The other workloads
 (causal window with null sinks, top-k prefill over a shared K=V cache, top-k
-decode with split-K and merge) are timed the same way and reported inside the
-same JSON line under "workloads".
+decode with split-K and merge, the device-side top-k list builder, and the
+per-block attention mass at the prefill shape) are timed the same way and
+reported inside the same JSON line under "workloads".
 
 To keep the 256 MB last-level cache (MALL) from serving a step's inputs from
 the previous step, every workload rotates between input sets whose union is
@@ -173,6 +174,35 @@ class BuildIdxWorkload(Workload):
         sattn.build_topk_idxs(self.sp, self.q_len, out=self.out[i % 2], **self.args)
 
 
+class BlockMassWorkload(IndexedWorkload):
+    """Per-block attention mass (normalise with the merged lse, sum per block of list entries) at the
+    prefill shape: the lse of each input set comes from the attention run once while preparing."""
+
+    def __init__(self, device, name, case, block_keys, q_sets=3):
+        import torch
+
+        import sliding_window_attention_index_amd as sattn
+        super().__init__(device, name, case, [case.topk_idxs], q_sets=q_sets, bound="mfma")
+        self.block_keys = block_keys
+        B, M, H, D, N, K = case.dims
+        self.lse = [sattn.indexed_fwd(q, self.kv, self.idx[0], softmax_scale=case.scale, return_lse=True)[1]
+                    for q in self.qs]
+        nb = -(-K // block_keys)
+        self.mass = [torch.empty((B, M, H, nb), dtype=torch.float32, device=device) for _ in self.qs]
+        torch.cuda.synchronize()
+        # q, the lists, the lse and the masses once, plus each listed row once per query
+        valid = int(((case.topk_idxs >= 0) & (case.topk_idxs < N)).sum())
+        self.bytes = valid * D * 2 + B * M * H * D * 2 + B * M * K * 4 + B * M * H * 4 + B * M * H * nb * 4
+        self.flops = 2 * D * self.pairs  # q . k only
+        self.config.update(workload=name, block_keys=block_keys, blocks_per_list=nb)
+
+    def launch(self, i):
+        import sliding_window_attention_index_amd as sattn
+        j = i % len(self.qs)
+        sattn.block_mass(self.qs[j], self.kv, self.idx[0], self.lse[j], block_keys=self.block_keys,
+                         softmax_scale=self.case0.scale, out=self.mass[j])
+
+
 def build_workload(name, device):
     import workloads as W
     if name == "vision_window":
@@ -186,6 +216,8 @@ def build_workload(name, device):
     if name == "sparse_decode":
         c = W.sparse_decode_case(seed=0, index_sets=16)
         return IndexedWorkload(device, name, c, c.extra["idx_sets"], q_sets=1, bound="hbm")
+    if name == "sparse_prefill_block_mass":
+        return BlockMassWorkload(device, name, W.sparse_prefill_case(seed=0), 64)
     if name == "topk_idx_build":
         return BuildIdxWorkload(device, name, [24576], 8192, 128, 4, 8192)
     raise ValueError(name)
@@ -304,7 +336,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="vision_window",
                     choices=["vision_window", "causal_window_null", "sparse_prefill", "sparse_decode",
-                             "topk_idx_build"])
+                             "topk_idx_build", "sparse_prefill_block_mass"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-extra", action="store_true", help="time only the headline workload")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -333,7 +365,7 @@ def main():
     names = [args.workload]
     if not args.no_extra:
         names += [n for n in ("vision_window", "causal_window_null", "sparse_prefill", "sparse_decode",
-                              "topk_idx_build") if n != args.workload]
+                              "topk_idx_build", "sparse_prefill_block_mass") if n != args.workload]
     results = {}
     main_wl = None
     for name in names:

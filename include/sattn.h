@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define SATTN_ABI_VERSION 2
+#define SATTN_ABI_VERSION 3
 
 typedef enum {
   SATTN_OK = 0,
@@ -227,6 +227,52 @@ typedef struct {
 } sattn_build_idx_args;
 
 sattn_status sattn_build_topk_idxs(const sattn_build_idx_args *args, hipStream_t stream);
+
+/*
+ * Attention mass of each block of list entries, normalised by a given
+ * log-sum-exp (nano-vllm XAttention offload note, technical details: the
+ * third stage of the chunked estimate normalises with the global softmax
+ * statistics that the first two stages produced per chunk and merged, and
+ * sums per block).  Here the statistics are those of the indexed path, e.g.
+ * the lse that sattn_indexed_fwd (one pass, or split-K and merged) returns.
+ *
+ *   q, kv, topk_idxs, softmax_scale, sinks, sink_mode: as sattn_indexed_args
+ *   lse        [batch, q_len, num_heads] fp32 natural log: the normaliser
+ *   block_keys entries per block (>= 1); block c of a list is entries
+ *              [c * block_keys, (c + 1) * block_keys)
+ *   mass       [batch, q_len, num_heads, ceil(topk / block_keys)] fp32
+ *              (written, every element)
+ *
+ *   mass[b, t, h, c] = sum over valid entries k of block c (0 <= idx < kv_len)
+ *                      of exp(softmax_scale * q[b, t, h] . kv[b, idx] + bias - lse[b, t, h]),
+ *   bias = sinks[h] for cache row 0 under KEY0_BIAS, else 0.  A null sink
+ *   belongs to no block: with the lse of the same list, the masses of a row
+ *   plus exp(sinks[h] - lse) sum to 1 (without a null sink they sum to 1).
+ *   A block with no valid entry gets 0; lse = -inf with a valid entry gives
+ *   +inf.  The fast path is bf16 with head_dim 64 or 128, num_heads a
+ *   multiple of 32, block_keys a multiple of 32 and softmax_scale > 0; other
+ *   shapes (fp32 among them) take a generic kernel.
+ */
+typedef struct {
+  sattn_dtype dtype;
+  const void *q;
+  const void *kv;
+  const int32_t *topk_idxs;
+  const float *lse;
+  float *mass;
+  int32_t batch;
+  int32_t q_len;
+  int32_t num_heads;
+  int32_t head_dim;
+  int32_t kv_len;
+  int32_t topk;
+  int32_t block_keys;
+  float softmax_scale;
+  const float *sinks;
+  sattn_sink_mode sink_mode;
+} sattn_block_mass_args;
+
+sattn_status sattn_block_mass(const sattn_block_mass_args *args, hipStream_t stream);
 
 sattn_status sattn_window_fwd(const sattn_window_args *args, hipStream_t stream);
 sattn_status sattn_indexed_fwd(const sattn_indexed_args *args, hipStream_t stream);

@@ -76,8 +76,9 @@ def block_mass(q, kv, topk_idxs, lse, *, scale: float, block_keys: int, sinks=No
     q [B, M, H, D], kv [B, N, D], topk_idxs [B, M, K], lse [B, M, H] (natural log).
     Returns float64 [B*M or len(rows), H, ceil(K / block_keys)].
     """
-    qf = np.asarray(q, dtype=np.float64) if not hasattr(q, "float") else q.float().numpy().astype(np.float64)
-    kvf = np.asarray(kv, dtype=np.float64) if not hasattr(kv, "float") else kv.float().numpy().astype(np.float64)
+    # bf16 / fp32 values are exact in fp32; rows are widened to fp64 when used
+    qf = np.asarray(q, dtype=np.float32) if not hasattr(q, "float") else q.float().numpy()
+    kvf = np.asarray(kv, dtype=np.float32) if not hasattr(kv, "float") else kv.float().numpy()
     idx = np.asarray(topk_idxs)
     ls = np.asarray(lse, dtype=np.float64)
     B, M, H, D = qf.shape
@@ -88,12 +89,12 @@ def block_mass(q, kv, topk_idxs, lse, *, scale: float, block_keys: int, sinks=No
     out = np.zeros((len(flat), H, nb), dtype=np.float64)
     for i, r in enumerate(flat):
         b, t = divmod(r, M)
-        for k in range(K):
-            x = int(idx[b, t, k])
-            if x < 0 or x >= N:
-                continue
-            logit = scale * (qf[b, t] @ kvf[b, x])  # [H]
-            if sink_mode == 1 and x == 0:
-                logit = logit + snk
-            out[i, :, k // block_keys] += np.exp(logit - ls[b, t])
+        ks = idx[b, t].astype(np.int64)
+        pos = np.nonzero((ks >= 0) & (ks < N))[0]  # list positions of the valid entries
+        x = ks[pos]                                # their cache rows
+        logit = scale * (qf[b, t].astype(np.float64) @ kvf[b, x].astype(np.float64).T)  # [H, n_valid]
+        if sink_mode == 1:
+            logit[:, x == 0] += snk[:, None]
+        e = np.exp(logit - ls[b, t][:, None])
+        np.add.at(out[i], (slice(None), pos // block_keys), e)  # entry k goes to block k // block_keys
     return out

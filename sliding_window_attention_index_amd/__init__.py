@@ -10,6 +10,7 @@ built, importing works but every call raises.
     o = indexed_fwd(q, kv, topk_idxs, sinks=sinks, sink_mode="null", num_splits=8)
     o = merge_lse(part_o, part_lse, sinks=sinks, sink_mode="null")
     idx = build_topk_idxs(start_pos, q_len, window=128, ratio=4, n_comp=8192)
+    mass = block_mass(q, kv, idx, lse, block_keys=64)   # lse from indexed_fwd(..., return_lse=True)
 """
 from __future__ import annotations
 
@@ -19,7 +20,8 @@ import os
 
 import torch  # loads the HIP runtime libsattn links against
 
-__all__ = ["window_fwd", "indexed_fwd", "merge_lse", "build_topk_idxs", "indexed_workspace_size", "SattnError",
+__all__ = ["window_fwd", "indexed_fwd", "merge_lse", "build_topk_idxs", "block_mass", "indexed_workspace_size",
+           "SattnError",
            "library_path", "load_library", "abi_version", "SINK_MODES"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -66,6 +68,15 @@ class _BuildIdxArgs(ctypes.Structure):
                 ("n_comp", ctypes.c_int32)]
 
 
+class _BlockMassArgs(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int), ("q", ctypes.c_void_p), ("kv", ctypes.c_void_p),
+                ("topk_idxs", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("mass", ctypes.c_void_p),
+                ("batch", ctypes.c_int32), ("q_len", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("kv_len", ctypes.c_int32), ("topk", ctypes.c_int32),
+                ("block_keys", ctypes.c_int32), ("softmax_scale", ctypes.c_float), ("sinks", ctypes.c_void_p),
+                ("sink_mode", ctypes.c_int)]
+
+
 _LIB = None
 
 
@@ -88,6 +99,8 @@ def load_library(path: str | None = None):
     lib.sattn_merge_lse.restype = ctypes.c_int
     lib.sattn_build_topk_idxs.argtypes = [ctypes.POINTER(_BuildIdxArgs), P]
     lib.sattn_build_topk_idxs.restype = ctypes.c_int
+    lib.sattn_block_mass.argtypes = [ctypes.POINTER(_BlockMassArgs), P]
+    lib.sattn_block_mass.restype = ctypes.c_int
     lib.sattn_indexed_workspace_size.argtypes = [ctypes.c_int32] * 5
     lib.sattn_indexed_workspace_size.restype = ctypes.c_size_t
     lib.sattn_status_string.argtypes = [ctypes.c_int]
@@ -254,4 +267,46 @@ def build_topk_idxs(start_pos, q_len: int, *, window: int, ratio: int, n_comp: i
     st = _lib_handle().sattn_build_topk_idxs(ctypes.byref(a), _stream(dev))
     if st != 0:
         raise SattnError(st, "sattn_build_topk_idxs")
+    return out
+
+
+def block_mass(q, kv, topk_idxs, lse, *, block_keys: int, softmax_scale: float | None = None, sinks=None,
+               sink_mode="none", out=None):
+    """Attention mass per block of `block_keys` list entries, normalised by `lse` (see include/sattn.h,
+    sattn_block_mass_args).
+
+    q [B,M,H,D], kv [B,N,D] (bf16 or fp32), topk_idxs int32 [B,M,K], lse fp32 [B,M,H] (natural log,
+    e.g. from indexed_fwd(..., return_lse=True)).  Returns fp32 [B, M, H, ceil(K / block_keys)].
+    """
+    dev = q.device
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    _check_dev("q", q, dev, dt)
+    _check_dev("kv", kv, dev, dt)
+    _check_dev("topk_idxs", topk_idxs, dev, torch.int32)
+    _check_dev("lse", lse, dev, torch.float32)
+    B, M, H, D = q.shape
+    N = kv.shape[1]
+    K = topk_idxs.shape[2]
+    if kv.shape != (B, N, D) or topk_idxs.shape[:2] != (B, M) or lse.shape != (B, M, H):
+        raise ValueError("kv must be [B, N, D], topk_idxs [B, M, K] and lse [B, M, H]")
+    if block_keys < 1:
+        raise ValueError("block_keys must be >= 1")
+    mode = _sink_mode(sink_mode, sinks)
+    if sinks is not None:
+        _check_dev("sinks", sinks, dev, torch.float32)
+    nb = -(-K // block_keys)
+    if out is None:
+        out = torch.empty((B, M, H, nb), dtype=torch.float32, device=dev)
+    else:
+        _check_dev("out", out, dev, torch.float32)
+        if tuple(out.shape) != (B, M, H, nb):
+            raise ValueError(f"out must have shape {(B, M, H, nb)}")
+    a = _BlockMassArgs(_DTYPES[dt], _ptr(q), _ptr(kv), _ptr(topk_idxs), _ptr(lse), _ptr(out), B, M, H, D, N, K,
+                       int(block_keys), float(1.0 / math.sqrt(D) if softmax_scale is None else softmax_scale),
+                       _ptr(sinks) if mode else None, mode)
+    st = _lib_handle().sattn_block_mass(ctypes.byref(a), _stream(dev))
+    if st != 0:
+        raise SattnError(st, "sattn_block_mass")
     return out

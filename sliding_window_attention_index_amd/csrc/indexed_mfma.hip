@@ -23,6 +23,13 @@
 //   * Online softmax with a lazy rescale (only when the running maximum grows
 //     by more than 2^8); the output goes through LDS so that it is written as
 //     whole rows (the 32 heads of a query are one contiguous stretch).
+//
+// Block-mass instantiation (kMass): the same gather and S^T product, then
+// instead of the softmax and PV each logit becomes exp2(s * c - lse * log2 e)
+// against a given log-sum-exp and the lane sums are written per block of
+// `block_keys` list entries (nano-vllm XAttention offload note, technical
+// details: the third stage normalises with the merged global statistics and
+// sums per block).  No V read, no accumulator, no epilogue.
 #include "lds_tile.hpp"
 #include "sattn_device.hpp"
 #include "sattn_kernels.hpp"
@@ -48,7 +55,7 @@ __device__ __forceinline__ int ds_read_i32(uint32_t addr) {
   return r;
 }
 
-template <int D, int NT>
+template <int D, int NT, bool kMass>
 __global__ __launch_bounds__(256) void indexed_fwd_mfma(IndexedParams p) {
   using Tile = SwizzledTile<D>;
   constexpr int S = D / 16;                  // MFMA steps over head_dim
@@ -75,7 +82,7 @@ __global__ __launch_bounds__(256) void indexed_fwd_mfma(IndexedParams p) {
   const int head0 = hg * 32;
   const bool partial = p.num_parts > 1;
   const bool key0 = p.sink_mode == kSinkKey0;
-  const bool null_sink = !partial && p.sink_mode == kSinkNull;
+  const bool null_sink = !kMass && !partial && p.sink_mode == kSinkNull;
 
   // B operand of S^T: q[bt, head0 + n, h*D/2 + 8s .. +8] (logical chunk h*S + s of the row).
   bf16x8 qf[S];
@@ -87,9 +94,19 @@ __global__ __launch_bounds__(256) void indexed_fwd_mfma(IndexedParams p) {
   const float c = p.scale_log2;  // > 0 on this path
   const float sink_raw = p.sinks ? p.sinks[head0 + n] * kLog2e / c : 0.0f;  // raw logit units
 
-  f32x16 acc[DB];
+  f32x16 acc[kMass ? 1 : DB];  // unused by the block-mass instantiation
+  if constexpr (!kMass) {
 #pragma unroll
-  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+    for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+  }
+  // Block mass: -lse in base 2 (an lse of -inf makes every valid entry +inf, as exp(s - lse)
+  // does; a finite stand-in keeps the masked -inf logits at exp2(-inf) = 0), and this lane's
+  // share of the current block's sum.
+  float neg_lse2 = 0.0f, bin_sum = 0.0f;
+  if constexpr (kMass) {
+    const float l = p.lse_in[bt * H + head0 + n];
+    neg_lse2 = l == kNegInf ? 3.0e38f : -l * kLog2e;
+  }
   RowSoftmax rs;
   rs.m = null_sink ? sink_raw : kNegInf;
   rs.l = (null_sink && h == 0) ? 1.0f : 0.0f;  // the pair of lanes sharing a head splits l
@@ -155,37 +172,54 @@ __global__ __launch_bounds__(256) void indexed_fwd_mfma(IndexedParams p) {
 #pragma unroll
     for (int s = 0; s < S; ++s)
       st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[s]), qf[s], st, 0, 0, 0);
-    uint32_t vb = vbase + slot * Tile::kBytes;
-    asm volatile("" : "+v"(vb));
-    u32x2 vr[4 * DB];
+    if constexpr (kMass) {
+      if (zmask) bias_block(st, zmask, h, sink_raw);
+      if (vmask != 0xffffffffu) mask_block(st, vmask, h);
+      float e0 = 0.0f, e1 = 0.0f;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      vr[db * 2] = ds_read_tr_b16<0>(vb ^ (64u * db));
-      vr[db * 2 + 1] = ds_read_tr_b16<kRow8>(vb ^ (64u * db + 16u));
-      vr[2 * DB + db * 2] = ds_read_tr_b16<2 * kRow8>(vb ^ (64u * db));
-      vr[2 * DB + db * 2 + 1] = ds_read_tr_b16<3 * kRow8>(vb ^ (64u * db + 16u));
-    }
-    // Accumulator element r of lane (n, h) is key 8*(r/4) + 4h + r%4 of head n.
-    if (zmask) bias_block(st, zmask, h, sink_raw);
-    if (vmask != 0xffffffffu) mask_block(st, vmask, h);
-    float alpha;
-    if (softmax_need_rescale(rs, block_max(st), c, alpha)) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db) acc[db] *= alpha;
-    }
-    bf16x8 pb[2];
-    softmax_probs(st, rs, c, pb);
-    lgkm_fence<0>(vr);
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+      for (int r = 0; r < 16; r += 2) {
+        e0 += fast_exp2(fmaf(st[r], c, neg_lse2));
+        e1 += fast_exp2(fmaf(st[r + 1], c, neg_lse2));
+      }
+      bin_sum += e0 + e1;
+    } else {
+      uint32_t vb = vbase + slot * Tile::kBytes;
+      asm volatile("" : "+v"(vb));
+      u32x2 vr[4 * DB];
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const u32x2 ra = vr[(tt * DB + db) * 2], rb = vr[(tt * DB + db) * 2 + 1];
-        const u32x4 av = {ra[0], ra[1], rb[0], rb[1]};
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pb[tt], acc[db], 0, 0, 0);
+        vr[db * 2] = ds_read_tr_b16<0>(vb ^ (64u * db));
+        vr[db * 2 + 1] = ds_read_tr_b16<kRow8>(vb ^ (64u * db + 16u));
+        vr[2 * DB + db * 2] = ds_read_tr_b16<2 * kRow8>(vb ^ (64u * db));
+        vr[2 * DB + db * 2 + 1] = ds_read_tr_b16<3 * kRow8>(vb ^ (64u * db + 16u));
       }
+      // Accumulator element r of lane (n, h) is key 8*(r/4) + 4h + r%4 of head n.
+      if (zmask) bias_block(st, zmask, h, sink_raw);
+      if (vmask != 0xffffffffu) mask_block(st, vmask, h);
+      float alpha;
+      if (softmax_need_rescale(rs, block_max(st), c, alpha)) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+      }
+      bf16x8 pb[2];
+      softmax_probs(st, rs, c, pb);
+      lgkm_fence<0>(vr);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const u32x2 ra = vr[(tt * DB + db) * 2], rb = vr[(tt * DB + db) * 2 + 1];
+          const u32x4 av = {ra[0], ra[1], rb[0], rb[1]};
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pb[tt], acc[db], 0, 0, 0);
+        }
+    }
   };
 
+  // Block mass: blocks of block_keys entries are whole runs of 32-entry tiles (block_keys % 32 == 0
+  // and every slice starts on a block boundary); `bin_left` tiles of the current block remain.
+  const int tiles_per_bin = kMass ? p.block_keys / kBlockKeys : 1;
+  int bin = kMass ? kb / p.block_keys : 0;
+  int bin_left = tiles_per_bin;
   for (int c0 = kb; c0 < ke; c0 += kIdxCap) {
     const int cend = min(ke, c0 + kIdxCap);
     const int nblk = (cend - c0 + kBlockKeys - 1) / kBlockKeys;
@@ -230,59 +264,70 @@ __global__ __launch_bounds__(256) void indexed_fwd_mfma(IndexedParams p) {
       const uint32_t vmask = static_cast<uint32_t>(__ballot(valid));
       const uint32_t zmask = key0 ? static_cast<uint32_t>(__ballot(valid && x == 0)) : 0u;
       if (vmask != 0u) compute(j & (NT - 1), vmask, zmask);
+      if constexpr (kMass) {
+        if (--bin_left == 0 || (j == nblk - 1 && cend == ke)) {  // the block ends with this tile
+          const float tot = halves_sum(bin_sum);
+          if (h == 0) p.mass[(bt * H + head0 + n) * p.n_bins + bin] = tot;
+          bin_sum = 0.0f;
+          ++bin;
+          bin_left = tiles_per_bin;
+        }
+      }
       if (j + NT < nblk) issue_block(j + NT);  // the slot's reads are done (lgkm fences in compute)
     }
   }
 
-  // Epilogue: o = acc / l, lse = ln(2) * (m + log2 l).  Lane (n, h) holds dims 32db + 8j + 4h + {0..3}
-  // of head n.  Each 32-dim block goes through the wave's first tile as scaled fp32 (16-byte chunk
-  // q of row r at q ^ (r & 7)) and comes back as 8 consecutive dims per lane.
-  const float l_tot = halves_sum(rs.l);
-  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  const float lse_v = l_tot > 0.0f ? (rs.m * c + log2f(l_tot)) * kLn2 : kNegInf;
-  const int64_t row0 = partial ? (static_cast<int64_t>(part) * BM + bt) * H + head0 : bt * H + head0;
-  const int rl = lane >> 2, q4 = lane & 3;
+  if constexpr (!kMass) {
+    // Epilogue: o = acc / l, lse = ln(2) * (m + log2 l).  Lane (n, h) holds dims 32db + 8j + 4h + {0..3}
+    // of head n.  Each 32-dim block goes through the wave's first tile as scaled fp32 (16-byte chunk
+    // q of row r at q ^ (r & 7)) and comes back as 8 consecutive dims per lane.
+    const float l_tot = halves_sum(rs.l);
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    const float lse_v = l_tot > 0.0f ? (rs.m * c + log2f(l_tot)) * kLn2 : kNegInf;
+    const int64_t row0 = partial ? (static_cast<int64_t>(part) * BM + bt) * H + head0 : bt * H + head0;
+    const int rl = lane >> 2, q4 = lane & 3;
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
+    for (int db = 0; db < DB; ++db) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const u32x4 w = {__float_as_uint(acc[db][4 * j] * inv), __float_as_uint(acc[db][4 * j + 1] * inv),
-                       __float_as_uint(acc[db][4 * j + 2] * inv), __float_as_uint(acc[db][4 * j + 3] * inv)};
-      ds_write_b128<0>(ring_addr + n * 128 + (((2 * j + h) ^ (n & 7)) << 4), w);
-    }
+      for (int j = 0; j < 4; ++j) {
+        const u32x4 w = {__float_as_uint(acc[db][4 * j] * inv), __float_as_uint(acc[db][4 * j + 1] * inv),
+                         __float_as_uint(acc[db][4 * j + 2] * inv), __float_as_uint(acc[db][4 * j + 3] * inv)};
+        ds_write_b128<0>(ring_addr + n * 128 + (((2 * j + h) ^ (n & 7)) << 4), w);
+      }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = 16 * i + rl;  // head head0 + r
-      u32x4 x[2];
-      x[0] = ds_read_b128<0>(ring_addr + r * 128 + (((2 * q4) ^ (r & 7)) << 4));
-      x[1] = ds_read_b128<0>(ring_addr + r * 128 + (((2 * q4 + 1) ^ (r & 7)) << 4));
-      lgkm_fence<0>(x);
-      const int64_t e0 = (row0 + r) * D + 32 * db + 8 * q4;
-      if (partial) {
-        *reinterpret_cast<u32x4 *>(p.part_o + e0) = x[0];
-        *reinterpret_cast<u32x4 *>(p.part_o + e0 + 4) = x[1];
-      } else {
-        const bf16x8 v = {static_cast<__bf16>(__uint_as_float(x[0][0])), static_cast<__bf16>(__uint_as_float(x[0][1])),
-                          static_cast<__bf16>(__uint_as_float(x[0][2])), static_cast<__bf16>(__uint_as_float(x[0][3])),
-                          static_cast<__bf16>(__uint_as_float(x[1][0])), static_cast<__bf16>(__uint_as_float(x[1][1])),
-                          static_cast<__bf16>(__uint_as_float(x[1][2])), static_cast<__bf16>(__uint_as_float(x[1][3]))};
-        *reinterpret_cast<bf16x8 *>(static_cast<__bf16 *>(p.o) + e0) = v;
+      for (int i = 0; i < 2; ++i) {
+        const int r = 16 * i + rl;  // head head0 + r
+        u32x4 x[2];
+        x[0] = ds_read_b128<0>(ring_addr + r * 128 + (((2 * q4) ^ (r & 7)) << 4));
+        x[1] = ds_read_b128<0>(ring_addr + r * 128 + (((2 * q4 + 1) ^ (r & 7)) << 4));
+        lgkm_fence<0>(x);
+        const int64_t e0 = (row0 + r) * D + 32 * db + 8 * q4;
+        if (partial) {
+          *reinterpret_cast<u32x4 *>(p.part_o + e0) = x[0];
+          *reinterpret_cast<u32x4 *>(p.part_o + e0 + 4) = x[1];
+        } else {
+          const bf16x8 v = {static_cast<__bf16>(__uint_as_float(x[0][0])), static_cast<__bf16>(__uint_as_float(x[0][1])),
+                            static_cast<__bf16>(__uint_as_float(x[0][2])), static_cast<__bf16>(__uint_as_float(x[0][3])),
+                            static_cast<__bf16>(__uint_as_float(x[1][0])), static_cast<__bf16>(__uint_as_float(x[1][1])),
+                            static_cast<__bf16>(__uint_as_float(x[1][2])), static_cast<__bf16>(__uint_as_float(x[1][3]))};
+          *reinterpret_cast<bf16x8 *>(static_cast<__bf16 *>(p.o) + e0) = v;
+        }
       }
     }
-  }
-  if (h == 0) {
-    if (partial) p.part_lse[row0 + n] = lse_v;
-    else if (p.lse) p.lse[row0 + n] = lse_v;
+    if (h == 0) {
+      if (partial) p.part_lse[row0 + n] = lse_v;
+      else if (p.lse) p.lse[row0 + n] = lse_v;
+    }
   }
 }
 
-template <int D, int NT>
+template <int D, int NT, bool kMass>
 hipError_t launch(const IndexedParams &p, hipStream_t stream) {
   const int n_hg = p.num_heads / 32;
   const int64_t tasks = static_cast<int64_t>(p.batch) * p.q_len * n_hg * p.num_parts;
   const int64_t blocks = (tasks + 3) / 4;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((indexed_fwd_mfma<D, NT>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((indexed_fwd_mfma<D, NT, kMass>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -299,8 +344,19 @@ hipError_t launch_indexed_mfma(const IndexedParams &p, hipStream_t stream) {
   // Few tasks (decode-like): one workgroup per CU anyway, so each wave keeps four blocks in flight.
   const int64_t tasks = static_cast<int64_t>(p.batch) * p.q_len * (p.num_heads / 32) * p.num_parts;
   const bool deep = tasks < 4096;
-  if (p.head_dim == 128) return deep ? launch<128, 4>(p, stream) : launch<128, 2>(p, stream);
-  return deep ? launch<64, 4>(p, stream) : launch<64, 2>(p, stream);
+  if (p.head_dim == 128) return deep ? launch<128, 4, false>(p, stream) : launch<128, 2, false>(p, stream);
+  return deep ? launch<64, 4, false>(p, stream) : launch<64, 2, false>(p, stream);
+}
+
+bool block_mass_mfma_supported(const IndexedParams &p) {
+  return indexed_mfma_supported(p) && p.block_keys % kBlockKeys == 0;
+}
+
+hipError_t launch_block_mass_mfma(const IndexedParams &p, hipStream_t stream) {
+  const int64_t tasks = static_cast<int64_t>(p.batch) * p.q_len * (p.num_heads / 32) * p.num_parts;
+  const bool deep = tasks < 4096;
+  if (p.head_dim == 128) return deep ? launch<128, 4, true>(p, stream) : launch<128, 2, true>(p, stream);
+  return deep ? launch<64, 4, true>(p, stream) : launch<64, 2, true>(p, stream);
 }
 
 }  // namespace sattn

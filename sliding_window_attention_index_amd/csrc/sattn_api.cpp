@@ -175,7 +175,7 @@ sattn_status sattn_indexed_fwd(const sattn_indexed_args *a, hipStream_t stream) 
       (a->sinks && !aligned4(a->sinks)))
     return SATTN_ERR_ALIGNMENT;
 
-  sattn::IndexedParams p;
+  sattn::IndexedParams p = {};
   p.q = a->q;
   p.kv = a->kv;
   p.idx = a->topk_idxs;
@@ -230,6 +230,59 @@ sattn_status sattn_indexed_fwd(const sattn_indexed_args *a, hipStream_t stream) 
   m.o = a->o;
   m.lse = a->lse;
   return launch_status(sattn::launch_merge(m, stream));
+}
+
+sattn_status sattn_block_mass(const sattn_block_mass_args *a, hipStream_t stream) {
+  if (!a) return SATTN_ERR_NULL_PTR;
+  if (!valid_dtype(a->dtype)) return SATTN_ERR_DTYPE;
+  if (!valid_sink(a->sink_mode)) return SATTN_ERR_ARG;
+  if (a->batch < 0 || a->q_len < 0 || a->num_heads <= 0 || a->kv_len < 0 || a->topk < 0 || a->block_keys < 1)
+    return SATTN_ERR_SHAPE;
+  if (sattn_status s = head_dim_status(a->head_dim)) return s;
+  if (!isfinite(a->softmax_scale)) return SATTN_ERR_ARG;
+  const int64_t rows = static_cast<int64_t>(a->batch) * a->q_len;
+  if (rows == 0 || a->topk == 0) return SATTN_OK;  // no block to write
+  if (rows > INT32_MAX) return SATTN_ERR_UNSUPPORTED;
+  if (!a->q || !a->topk_idxs || !a->lse || !a->mass || (a->kv_len > 0 && !a->kv)) return SATTN_ERR_NULL_PTR;
+  if (a->sink_mode == SATTN_SINK_KEY0_BIAS && !a->sinks) return SATTN_ERR_NULL_PTR;
+  if (!aligned16(a->q) || (a->kv && !aligned16(a->kv)) || !aligned4(a->topk_idxs) || !aligned4(a->lse) ||
+      !aligned4(a->mass) || (a->sinks && !aligned4(a->sinks)))
+    return SATTN_ERR_ALIGNMENT;
+
+  sattn::IndexedParams p = {};
+  p.q = a->q;
+  p.kv = a->kv;
+  p.idx = a->topk_idxs;
+  p.batch = a->batch;
+  p.q_len = a->q_len;
+  p.num_heads = a->num_heads;
+  p.head_dim = a->head_dim;
+  p.kv_len = a->kv_len;
+  p.topk = a->topk;
+  p.scale_log2 = a->softmax_scale * 1.4426950408889634f;
+  // Only the key-0 bias touches a block; a null sink belongs to none.
+  p.sinks = a->sink_mode == SATTN_SINK_KEY0_BIAS ? a->sinks : nullptr;
+  p.sink_mode = a->sink_mode == SATTN_SINK_KEY0_BIAS ? SATTN_SINK_KEY0_BIAS : SATTN_SINK_NONE;
+  p.lse_in = a->lse;
+  p.mass = a->mass;
+  p.block_keys = a->block_keys;
+  p.n_bins = static_cast<int>((static_cast<int64_t>(a->topk) + a->block_keys - 1) / a->block_keys);
+  p.num_parts = 1;
+  p.part_len = a->topk;
+  if (a->dtype == SATTN_BF16 && sattn::block_mass_mfma_supported(p)) {
+    // Blocks need no merge, so a list is cut into slices of whole blocks whenever that brings the
+    // wave count near 4096 (a few per SIMD): decode-like shapes have few queries and long lists.
+    const int64_t tasks = rows * (a->num_heads / 32);
+    int64_t per = (4096 + tasks - 1) / tasks;  // slices wanted per list
+    if (per > p.n_bins) per = p.n_bins;
+    if (per > 1) {
+      const int64_t bins_per_part = (p.n_bins + per - 1) / per;
+      p.part_len = static_cast<int>(bins_per_part * a->block_keys);
+      p.num_parts = static_cast<int>((p.n_bins + bins_per_part - 1) / bins_per_part);
+    }
+    return launch_status(sattn::launch_block_mass_mfma(p, stream));
+  }
+  return launch_status(sattn::launch_block_mass_valu(p, a->dtype == SATTN_F32 ? sattn::kF32 : sattn::kBF16, stream));
 }
 
 }  // extern "C"

@@ -46,6 +46,10 @@ struct IndexedParams {
   int part_len;         // entries per slice (ceil(topk / num_parts))
   float *part_o;        // [num_parts, B*M, H, D] when num_parts > 1
   float *part_lse;      // [num_parts, B*M, H]
+  // Block-mass launches (o, lse and part_* unused; part_len is a multiple of block_keys):
+  const float *lse_in;  // [B*M, H] natural log, the normaliser
+  float *mass;          // [B*M, H, n_bins]
+  int block_keys, n_bins;
 };
 
 struct MergeParams {
@@ -70,5 +74,10 @@ bool indexed_mfma_supported(const IndexedParams &p);
 hipError_t launch_indexed_mfma(const IndexedParams &p, hipStream_t stream);
 
 hipError_t launch_build_topk_idxs(const BuildIdxParams &p, hipStream_t stream);
+
+// Per-block attention mass of the lists (IndexedParams block-mass fields).
+hipError_t launch_block_mass_valu(const IndexedParams &p, int elem_type, hipStream_t stream);
+bool block_mass_mfma_supported(const IndexedParams &p);
+hipError_t launch_block_mass_mfma(const IndexedParams &p, hipStream_t stream);
 
 }  // namespace sattn

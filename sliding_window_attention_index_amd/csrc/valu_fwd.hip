@@ -176,6 +176,57 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void indexed_fwd_valu(IndexedP
   }
 }
 
+// Attention mass per block of list entries, normalised by a given log-sum-exp (nano-vllm XAttention
+// offload note, technical details: the third stage normalises with the merged global statistics and
+// sums per block).  Generic shapes: one wave per (query, head); for block c the lanes take 64 of
+// its entries at a time, a valid entry contributes exp2(s - lse * log2(e)) with s its logit in base
+// 2 (key-0 bias included), and a wave sum gives the block's mass.  Every block is written.
+template <typename T>
+__global__ __launch_bounds__(64 * kWavesPerBlock) void block_mass_valu(IndexedParams p) {
+  __shared__ float q_lds[kWavesPerBlock][kMaxHeadDim];
+  const int wave = threadIdx.x >> 6;
+  const int lane = lane_id();
+  const int64_t BM = static_cast<int64_t>(p.batch) * p.q_len;
+  const int64_t bt = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave;
+  if (bt >= BM) return;
+  const int h = blockIdx.y;
+  const int D = p.head_dim, N = p.kv_len, K = p.topk, bk = p.block_keys;
+  const int64_t b = bt / p.q_len;
+  const int64_t rh = bt * p.num_heads + h;
+  const T *qrow = static_cast<const T *>(p.q) + rh * D;
+  float *ql = q_lds[wave];
+  for (int d = lane; d < D; d += 64) ql[d] = load_elem(qrow + d);
+  wave_lds_sync();
+  const int32_t *list = p.idx + bt * K;
+  const T *kvb = static_cast<const T *>(p.kv) + b * static_cast<int64_t>(N) * D;
+  const float lse2 = p.lse_in[rh] * kLog2e;
+  const float bias2 = p.sink_mode == kSinkKey0 ? p.sinks[h] * kLog2e : 0.0f;
+  float *out = p.mass + rh * p.n_bins;
+  for (int c = 0; c < p.n_bins; ++c) {
+    const int lo = c * bk, hi = min(K, lo + bk);
+    float part = 0.0f;
+    for (int base = lo; base < hi; base += 64) {
+      const int slot = base + lane;
+      const int x = slot < hi ? list[slot] : -1;
+      if (x >= 0 && x < N) {
+        const T *krow = kvb + static_cast<int64_t>(x) * D;
+        float dot = 0.0f;
+        for (int d = 0; d < D; d += 8) {
+          float kk[8];
+          load8(krow + d, kk);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) dot = fmaf(ql[d + i], kk[i], dot);
+        }
+        float s = dot * p.scale_log2;
+        if (x == 0) s += bias2;
+        part += fast_exp2(s - lse2);
+      }
+    }
+    const float tot = wave_sum(part);
+    if (lane == 0) out[c] = tot;
+  }
+}
+
 // Merge of per-chunk partial results: M = max(lse_c, sink), W = sum exp(lse_c - M) [+ exp(sink - M)].
 // One thread per (row, head, 4 consecutive dims): the parts' log-sum-exps first (maximum, then
 // weights), then every part's 16-byte slice of o in flight together.  [P3] technical details:
@@ -303,6 +354,16 @@ hipError_t launch_indexed_valu(const IndexedParams &p, int elem_type, hipStream_
     hipLaunchKernelGGL(indexed_fwd_valu<float>, grid, dim3(64 * kWavesPerBlock), 0, stream, p);
   else
     hipLaunchKernelGGL(indexed_fwd_valu<__bf16>, grid, dim3(64 * kWavesPerBlock), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_mass_valu(const IndexedParams &p, int elem_type, hipStream_t stream) {
+  const int64_t BM = static_cast<int64_t>(p.batch) * p.q_len;
+  const dim3 grid(static_cast<unsigned>((BM + kWavesPerBlock - 1) / kWavesPerBlock), p.num_heads);
+  if (elem_type == kF32)
+    hipLaunchKernelGGL(block_mass_valu<float>, grid, dim3(64 * kWavesPerBlock), 0, stream, p);
+  else
+    hipLaunchKernelGGL(block_mass_valu<__bf16>, grid, dim3(64 * kWavesPerBlock), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -11,7 +11,7 @@ import re
 import pytest
 
 import sliding_window_attention_index_amd as sattn
-from sliding_window_attention_index_amd import _BuildIdxArgs, _IndexedArgs, _MergeArgs, _WindowArgs
+from sliding_window_attention_index_amd import _BlockMassArgs, _BuildIdxArgs, _IndexedArgs, _MergeArgs, _WindowArgs
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sattn.h")
@@ -36,7 +36,7 @@ def _declared_functions():
 def test_header_functions_exported(lib):
     names = _declared_functions()
     assert set(names) == {"sattn_window_fwd", "sattn_indexed_fwd", "sattn_merge_lse", "sattn_build_topk_idxs",
-                          "sattn_indexed_workspace_size", "sattn_status_string", "sattn_abi_version"}
+                          "sattn_block_mass", "sattn_indexed_workspace_size", "sattn_status_string", "sattn_abi_version"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -179,3 +179,36 @@ def test_build_topk_idxs_empty_is_noop(lib):
     assert lib.sattn_build_topk_idxs(ctypes.byref(_build(batch=0, out=None, start_pos=None)), None) == OK
     assert lib.sattn_build_topk_idxs(ctypes.byref(_build(q_len=0, out=None)), None) == OK
     assert lib.sattn_build_topk_idxs(None, None) == NULL_PTR
+
+
+def _mass(**kw):
+    base = dict(dtype=0, q=FAKE, kv=FAKE, topk_idxs=FAKE, lse=FAKE, mass=FAKE, batch=1, q_len=8192, num_heads=32,
+                head_dim=128, kv_len=8320, topk=640, block_keys=64, softmax_scale=0.088, sinks=None, sink_mode=0)
+    base.update(kw)
+    return _BlockMassArgs(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=2), DTYPE),
+    (dict(sink_mode=3), ARG),
+    (dict(block_keys=0), SHAPE),
+    (dict(batch=-1), SHAPE),
+    (dict(num_heads=0), SHAPE),
+    (dict(head_dim=100), UNSUPPORTED),
+    (dict(softmax_scale=float("nan")), ARG),
+    (dict(lse=None), NULL_PTR),
+    (dict(mass=None), NULL_PTR),
+    (dict(topk_idxs=None), NULL_PTR),
+    (dict(sink_mode=1, sinks=None), NULL_PTR),
+    (dict(q=FAKE + 8), ALIGNMENT),
+    (dict(mass=FAKE + 2), ALIGNMENT),
+    (dict(lse=FAKE + 1), ALIGNMENT),
+])
+def test_block_mass_validation(lib, kw, status):
+    assert lib.sattn_block_mass(ctypes.byref(_mass(**kw)), None) == status
+
+
+def test_block_mass_empty_is_noop(lib):
+    assert lib.sattn_block_mass(ctypes.byref(_mass(batch=0, q=None, mass=None)), None) == OK
+    assert lib.sattn_block_mass(ctypes.byref(_mass(topk=0, mass=None)), None) == OK
+    assert lib.sattn_block_mass(None, None) == NULL_PTR

@@ -193,9 +193,10 @@ def test_block_mass_with_merged_statistics():
 
 
 MASS_MUTANTS = {
-    "bins_by_cache_row": ("out[i, :, k // block_keys]", "out[i, :, min(x, K - 1) // block_keys]"),
-    "key0_bias_dropped": ("logit = logit + snk", "logit = logit"),
-    "unscaled_logit": ("logit = scale * (qf[b, t] @ kvf[b, x])", "logit = (qf[b, t] @ kvf[b, x])"),
+    "bins_by_cache_row": ("(slice(None), pos // block_keys)", "(slice(None), np.minimum(x, K - 1) // block_keys)"),
+    "key0_bias_dropped": ("logit[:, x == 0] += snk[:, None]", "pass"),
+    "unscaled_logit": ("logit = scale * (qf", "logit = (qf"),
+    "lse_not_subtracted": ("np.exp(logit - ls[b, t][:, None])", "np.exp(logit)"),
 }
 
 
