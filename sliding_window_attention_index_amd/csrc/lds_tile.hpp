@@ -95,6 +95,20 @@ template <int OFF>
 __device__ __forceinline__ void ds_write_b128(uint32_t addr, u32x4 v) {
   asm volatile("ds_write_b128 %0, %1 offset:%2" ::"v"(addr), "v"(v), "i"(OFF));
 }
+template <int OFF>
+__device__ __forceinline__ void ds_write_b64(uint32_t addr, u32x2 v) {
+  asm volatile("ds_write_b64 %0, %1 offset:%2" ::"v"(addr), "v"(v), "i"(OFF));
+}
+// A buffer store of more than 64 bits reads its data registers after it issues, and a VALU write
+// of those registers right behind it changes what is stored; the compiler pads this case only when
+// the store's offset is not an SGPR.  Stores with an SGPR offset go through here: the data stays
+// live, and therefore unwritten, until two wait states after the store.
+__device__ __forceinline__ void buffer_store_b128_sgpr(u32x4 v, __amdgpu_buffer_rsrc_t rsrc, uint32_t voffset,
+                                                       uint32_t soffset) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, voffset, soffset, 0);
+  asm volatile("s_nop 1" ::"v"(v));
+}
+
 // s_waitcnt lgkmcnt(N) that the registers in `regs` depend on.
 template <int N, typename T, int M>
 __device__ __forceinline__ void lgkm_fence(T (&regs)[M]) {

@@ -276,8 +276,7 @@ __global__ __launch_bounds__(256) void window_fwd_mfma(WindowParams p, int tiles
                         static_cast<__bf16>(__uint_as_float(x[1][0])), static_cast<__bf16>(__uint_as_float(x[1][1])),
                         static_cast<__bf16>(__uint_as_float(x[1][2])), static_cast<__bf16>(__uint_as_float(x[1][3]))};
       const uint32_t uni = static_cast<uint32_t>(wq0 + (16 * i) / G) * q_tok + ((16 * i) % G) * D * 2 + db * 64;
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ors, vlane,
-                                             __builtin_amdgcn_readfirstlane(uni), 0);
+      buffer_store_b128_sgpr(__builtin_bit_cast(u32x4, v), ors, vlane, __builtin_amdgcn_readfirstlane(uni));
     }
   }
   if (p.lse && h == 0 && my_q < Lq)
