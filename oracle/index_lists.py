@@ -1,4 +1,5 @@
-"""CPU oracle for top-k list construction and per-block attention mass (test infrastructure).
+"""CPU oracle for top-k list construction, per-block attention mass and the compressor's gated
+pooling (test infrastructure).
 
 Only the test suite, ``__graft_entry__.smoke()`` and the benchmark's
 ``cpu_baseline`` leg may import this module; the product path never does.
@@ -97,4 +98,45 @@ def block_mass(q, kv, topk_idxs, lse, *, scale: float, block_keys: int, sinks=No
             logit[:, x == 0] += snk[:, None]
         e = np.exp(logit - ls[b, t][:, None])
         np.add.at(out[i], (slice(None), pos // block_keys), e)  # entry k goes to block k // block_keys
+    return out
+
+
+def compress_pool(kv, score, ape, *, ratio: int, overlap: bool) -> np.ndarray:
+    """Gated pooling of the compressor: one compressed row per complete window of `ratio` tokens.
+
+    Source: DeepSeek-V4 CSA/HCA article, §5.1 (compressed kv = sum over the window of kv_i times
+    softmax(score_i), the softmax taken over the window's tokens; the learned absolute position
+    term ape [ratio, coff * d] is added to the scores first; coff = 2 with overlap) and its
+    overlap-transform description (window i takes the previous window's tokens with the first d
+    features and its own tokens with the last d features).  Readings: the softmax is per feature;
+    window w holds tokens [w * ratio, (w + 1) * ratio); a trailing partial window is not
+    compressed; with overlap, window 0 has no previous window and its first half contributes
+    nothing (weight 0).
+
+    kv, score: [B, S, coff * d]; ape: [ratio, coff * d].  Returns float64 [B, S // ratio, d].
+    """
+    kvf = np.asarray(kv.float().numpy() if hasattr(kv, "float") else kv, dtype=np.float64)
+    scf = np.asarray(score.float().numpy() if hasattr(score, "float") else score, dtype=np.float64)
+    apf = np.asarray(ape.float().numpy() if hasattr(ape, "float") else ape, dtype=np.float64)
+    B, S, F = kvf.shape
+    coff = 2 if overlap else 1
+    d = F // coff
+    n_out = S // ratio
+    out = np.zeros((B, n_out, d), dtype=np.float64)
+    for b in range(B):
+        for w in range(n_out):
+            rows_kv, rows_sc = [], []  # one entry per (token, its feature half) in the window
+            if overlap and w > 0:
+                for i in range(ratio):
+                    t = (w - 1) * ratio + i
+                    rows_kv.append(kvf[b, t, :d])
+                    rows_sc.append(scf[b, t, :d] + apf[i, :d])
+            for i in range(ratio):
+                t = w * ratio + i
+                lo = d if overlap else 0
+                rows_kv.append(kvf[b, t, lo:lo + d])
+                rows_sc.append(scf[b, t, lo:lo + d] + apf[i, lo:lo + d])
+            sc = np.stack(rows_sc)                # [tokens, d]
+            e = np.exp(sc - sc.max(axis=0))
+            out[b, w] = (e * np.stack(rows_kv)).sum(axis=0) / e.sum(axis=0)
     return out
