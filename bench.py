@@ -7,8 +7,9 @@ already resident in HBM.  The headline workload is the vision-encoder window
 attention (16 sequences, lengths U[1024, 4096], 16 query / 8 KV heads,
 head_dim 128, symmetric window 128, key-0 sinks, bf16).  The other workloads
 (causal window with null sinks, top-k prefill over a shared K=V cache, top-k
-decode with split-K and merge, the device-side top-k list builder, and the
-per-block attention mass at the prefill shape) are timed the same way and
+decode with split-K and merge, the device-side top-k list builder, the
+per-block attention mass at the prefill shape, and the compressor pooling of the
+prefill sequence) are timed the same way and
 reported inside the same JSON line under "workloads".
 
 To keep the 256 MB last-level cache (MALL) from serving a step's inputs from
@@ -203,6 +204,41 @@ class BlockMassWorkload(IndexedWorkload):
                          softmax_scale=self.case0.scale, out=self.mass[j])
 
 
+class CompressWorkload(Workload):
+    """Compressor pooling of the prefill sequence: 32768 tokens, ratio 4 with overlap, D 128, bf16
+    -> 8192 compressed rows.  Eight input sets (268 MB) rotate so that the MALL does not serve a
+    launch's inputs from the previous one."""
+
+    def __init__(self, device, name, batch=1, seq_len=32768, head_dim=128, ratio=4, overlap=True, n_sets=8):
+        import torch
+        super().__init__(device)
+        self.name = name
+        self.bound = "hbm"
+        self.case0 = None
+        F = (2 if overlap else 1) * head_dim
+        g = torch.Generator().manual_seed(0)
+        self.sets = []
+        for _ in range(n_sets):
+            kv = torch.randn(batch, seq_len, F, generator=g).to(torch.bfloat16).to(device)
+            sc = (2.0 * torch.randn(batch, seq_len, F, generator=g)).to(torch.bfloat16).to(device)
+            self.sets.append((kv, sc))
+        self.ape = (0.5 * torch.randn(ratio, F, generator=g)).to(torch.bfloat16).to(device)
+        n_out = seq_len // ratio
+        self.out = torch.empty((batch, n_out, head_dim), dtype=torch.bfloat16, device=device)
+        self.ratio, self.overlap = ratio, overlap
+        self.bytes = 2 * batch * seq_len * F * 2 + ratio * F * 2 + batch * n_out * head_dim * 2
+        self.pairs = batch * n_out  # compressed rows written
+        self.flops = 0
+        self.unit = "compressed rows/s"
+        self.config = dict(workload=name, batch=batch, seq_len=seq_len, head_dim=head_dim, ratio=ratio,
+                           overlap=overlap, input_sets=n_sets)
+
+    def launch(self, i):
+        import sliding_window_attention_index_amd as sattn
+        kv, sc = self.sets[i % len(self.sets)]
+        sattn.compress_pool(kv, sc, self.ape, ratio=self.ratio, overlap=self.overlap, out=self.out)
+
+
 def build_workload(name, device):
     import workloads as W
     if name == "vision_window":
@@ -218,6 +254,8 @@ def build_workload(name, device):
         return IndexedWorkload(device, name, c, c.extra["idx_sets"], q_sets=1, bound="hbm")
     if name == "sparse_prefill_block_mass":
         return BlockMassWorkload(device, name, W.sparse_prefill_case(seed=0), 64)
+    if name == "compress_pool":
+        return CompressWorkload(device, name)
     if name == "topk_idx_build":
         return BuildIdxWorkload(device, name, [24576], 8192, 128, 4, 8192)
     raise ValueError(name)
@@ -336,7 +374,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="vision_window",
                     choices=["vision_window", "causal_window_null", "sparse_prefill", "sparse_decode",
-                             "topk_idx_build", "sparse_prefill_block_mass"])
+                             "topk_idx_build", "sparse_prefill_block_mass", "compress_pool"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-extra", action="store_true", help="time only the headline workload")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -365,7 +403,7 @@ def main():
     names = [args.workload]
     if not args.no_extra:
         names += [n for n in ("vision_window", "causal_window_null", "sparse_prefill", "sparse_decode",
-                              "topk_idx_build", "sparse_prefill_block_mass") if n != args.workload]
+                              "topk_idx_build", "sparse_prefill_block_mass", "compress_pool") if n != args.workload]
     results = {}
     main_wl = None
     for name in names:

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define SATTN_ABI_VERSION 3
+#define SATTN_ABI_VERSION 4
 
 typedef enum {
   SATTN_OK = 0,
@@ -273,6 +273,47 @@ typedef struct {
 } sattn_block_mass_args;
 
 sattn_status sattn_block_mass(const sattn_block_mass_args *args, hipStream_t stream);
+
+/*
+ * Gated pooling of the compressor (DeepSeek-V4 CSA/HCA article, §5.1: a compressed row is the
+ * sum over a window of kv_i * softmax(score_i), with the learned absolute position term ape
+ * added to the scores; with overlap, kv and score carry 2 * head_dim features per token and the
+ * overlap transform lets window i see the previous window's tokens through their first
+ * head_dim features and its own tokens through their last head_dim features).
+ *
+ *   kv, score  [batch, seq_len, coff * head_dim] dtype (coff = 2 if overlap, else 1): the
+ *              projected kv and gate scores of every token
+ *   ape        [ratio, coff * head_dim] dtype
+ *   out        compressed row w of batch b at out + (b * out_batch_stride + w) * head_dim,
+ *              w < seq_len / ratio (written); out_batch_stride >= seq_len / ratio rows, so out
+ *              may point at the compressed region of a [batch, window + n_comp, head_dim]
+ *              cache (out = cache + window * head_dim, stride window + n_comp)
+ *
+ *   Window w holds tokens [w * ratio, (w + 1) * ratio); a trailing partial window is not
+ *   compressed.  For every feature f < head_dim:
+ *     entries = {(kv[t][lo + f], score[t][lo + f] + ape[t - w * ratio][lo + f]) : t in window w}
+ *               with lo = head_dim if overlap else 0,
+ *             plus, with overlap and w > 0, {(kv[t][f], score[t][f] + ape[t - (w-1) * ratio][f]) :
+ *               t in window w - 1};
+ *     out[w][f] = sum over entries of kv * exp(s) / sum of exp(s).
+ *   Computed in fp32; out rounded to dtype.  head_dim must be a multiple of 8 and the tensors
+ *   16-byte aligned.
+ */
+typedef struct {
+  sattn_dtype dtype;
+  const void *kv;
+  const void *score;
+  const void *ape;
+  void *out;
+  int64_t out_batch_stride;
+  int32_t batch;
+  int32_t seq_len;
+  int32_t head_dim;
+  int32_t ratio;
+  int32_t overlap;
+} sattn_compress_args;
+
+sattn_status sattn_compress_pool(const sattn_compress_args *args, hipStream_t stream);
 
 sattn_status sattn_window_fwd(const sattn_window_args *args, hipStream_t stream);
 sattn_status sattn_indexed_fwd(const sattn_indexed_args *args, hipStream_t stream);

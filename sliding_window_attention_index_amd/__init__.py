@@ -11,6 +11,7 @@ built, importing works but every call raises.
     o = merge_lse(part_o, part_lse, sinks=sinks, sink_mode="null")
     idx = build_topk_idxs(start_pos, q_len, window=128, ratio=4, n_comp=8192)
     mass = block_mass(q, kv, idx, lse, block_keys=64)   # lse from indexed_fwd(..., return_lse=True)
+    rows = compress_pool(kv_proj, score_proj, ape, ratio=4, overlap=True)
 """
 from __future__ import annotations
 
@@ -20,7 +21,8 @@ import os
 
 import torch  # loads the HIP runtime libsattn links against
 
-__all__ = ["window_fwd", "indexed_fwd", "merge_lse", "build_topk_idxs", "block_mass", "indexed_workspace_size",
+__all__ = ["window_fwd", "indexed_fwd", "merge_lse", "build_topk_idxs", "block_mass", "compress_pool",
+           "indexed_workspace_size",
            "SattnError",
            "library_path", "load_library", "abi_version", "SINK_MODES"]
 
@@ -77,6 +79,13 @@ class _BlockMassArgs(ctypes.Structure):
                 ("sink_mode", ctypes.c_int)]
 
 
+class _CompressArgs(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int), ("kv", ctypes.c_void_p), ("score", ctypes.c_void_p), ("ape", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("out_batch_stride", ctypes.c_int64), ("batch", ctypes.c_int32),
+                ("seq_len", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("ratio", ctypes.c_int32),
+                ("overlap", ctypes.c_int32)]
+
+
 _LIB = None
 
 
@@ -101,6 +110,8 @@ def load_library(path: str | None = None):
     lib.sattn_build_topk_idxs.restype = ctypes.c_int
     lib.sattn_block_mass.argtypes = [ctypes.POINTER(_BlockMassArgs), P]
     lib.sattn_block_mass.restype = ctypes.c_int
+    lib.sattn_compress_pool.argtypes = [ctypes.POINTER(_CompressArgs), P]
+    lib.sattn_compress_pool.restype = ctypes.c_int
     lib.sattn_indexed_workspace_size.argtypes = [ctypes.c_int32] * 5
     lib.sattn_indexed_workspace_size.restype = ctypes.c_size_t
     lib.sattn_status_string.argtypes = [ctypes.c_int]
@@ -309,4 +320,47 @@ def block_mass(q, kv, topk_idxs, lse, *, block_keys: int, softmax_scale: float |
     st = _lib_handle().sattn_block_mass(ctypes.byref(a), _stream(dev))
     if st != 0:
         raise SattnError(st, "sattn_block_mass")
+    return out
+
+
+def compress_pool(kv, score, ape, *, ratio: int, overlap: bool, out=None):
+    """Compressed rows [B, S // ratio, d] of the compressor's gated pooling (see include/sattn.h,
+    sattn_compress_args).
+
+    kv, score [B, S, coff * d] and ape [ratio, coff * d] (bf16 or fp32; coff = 2 with overlap).
+    `out` may be any [B, n, d] tensor view with n >= S // ratio whose rows are contiguous (for
+    instance the compressed region cache[:, window:, :] of a cache); the first S // ratio rows of
+    each batch are written.
+    """
+    dev = kv.device
+    dt = kv.dtype
+    if dt not in _DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    _check_dev("kv", kv, dev, dt)
+    _check_dev("score", score, dev, dt)
+    _check_dev("ape", ape, dev, dt)
+    B, S, F = kv.shape
+    coff = 2 if overlap else 1
+    if score.shape != kv.shape or F % coff or tuple(ape.shape) != (ratio, F):
+        raise ValueError("score must be shaped like kv and ape [ratio, coff * d]")
+    d = F // coff
+    n_out = S // ratio
+    if out is None:
+        out = torch.empty((B, n_out, d), dtype=dt, device=dev)
+        stride = n_out
+    else:
+        if out.device != dev or out.dtype != dt:
+            raise ValueError(f"out must be {dt} on {dev}")
+        if out.dim() != 3 or out.shape[0] != B or out.shape[2] != d or out.shape[1] < n_out:
+            raise ValueError(f"out must be [{B}, >= {n_out}, {d}]")
+        if out.stride(2) != 1 or out.stride(1) != d:
+            raise ValueError("out rows must be contiguous")
+        stride = out.stride(0) // d if out.stride(0) % d == 0 else -1
+        if stride < n_out:
+            raise ValueError("out batch stride must be a whole number of rows >= S // ratio")
+    a = _CompressArgs(_DTYPES[dt], _ptr(kv), _ptr(score), _ptr(ape), _ptr(out), int(stride), B, S, d, int(ratio),
+                      1 if overlap else 0)
+    st = _lib_handle().sattn_compress_pool(ctypes.byref(a), _stream(dev))
+    if st != 0:
+        raise SattnError(st, "sattn_compress_pool")
     return out

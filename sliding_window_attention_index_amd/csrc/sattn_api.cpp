@@ -285,4 +285,32 @@ sattn_status sattn_block_mass(const sattn_block_mass_args *a, hipStream_t stream
   return launch_status(sattn::launch_block_mass_valu(p, a->dtype == SATTN_F32 ? sattn::kF32 : sattn::kBF16, stream));
 }
 
+sattn_status sattn_compress_pool(const sattn_compress_args *a, hipStream_t stream) {
+  if (!a) return SATTN_ERR_NULL_PTR;
+  if (!valid_dtype(a->dtype)) return SATTN_ERR_DTYPE;
+  if (a->overlap != 0 && a->overlap != 1) return SATTN_ERR_ARG;
+  if (a->batch < 0 || a->seq_len < 0 || a->ratio < 1) return SATTN_ERR_SHAPE;
+  if (a->head_dim <= 0) return SATTN_ERR_SHAPE;
+  if (a->head_dim % 8 != 0) return SATTN_ERR_UNSUPPORTED;
+  const int64_t n_out = a->seq_len / a->ratio;
+  if (a->out_batch_stride < n_out) return SATTN_ERR_SHAPE;
+  if (a->batch == 0 || n_out == 0) return SATTN_OK;
+  if (!a->kv || !a->score || !a->ape || !a->out) return SATTN_ERR_NULL_PTR;
+  if (!aligned16(a->kv) || !aligned16(a->score) || !aligned16(a->ape) || !aligned16(a->out))
+    return SATTN_ERR_ALIGNMENT;
+  if (static_cast<int64_t>(a->batch) * n_out * (a->head_dim / 8) > (int64_t(1) << 40)) return SATTN_ERR_UNSUPPORTED;
+  sattn::CompressParams p;
+  p.kv = a->kv;
+  p.score = a->score;
+  p.ape = a->ape;
+  p.out = a->out;
+  p.out_batch_stride = a->out_batch_stride;
+  p.batch = a->batch;
+  p.seq_len = a->seq_len;
+  p.head_dim = a->head_dim;
+  p.ratio = a->ratio;
+  p.overlap = a->overlap;
+  return launch_status(sattn::launch_compress_pool(p, a->dtype == SATTN_F32 ? sattn::kF32 : sattn::kBF16, stream));
+}
+
 }  // extern "C"

@@ -52,6 +52,15 @@ struct IndexedParams {
   int block_keys, n_bins;
 };
 
+// Compressor pooling (one compressed row per complete window of `ratio` tokens).
+struct CompressParams {
+  const void *kv, *score;  // [batch, seq_len, coff * head_dim]
+  const void *ape;         // [ratio, coff * head_dim]
+  void *out;               // row w of batch b at out + (b * out_batch_stride + w) * head_dim
+  int64_t out_batch_stride;
+  int batch, seq_len, head_dim, ratio, overlap;
+};
+
 struct MergeParams {
   const float *part_o, *part_lse;
   int num_parts, rows, num_heads, head_dim;
@@ -74,6 +83,7 @@ bool indexed_mfma_supported(const IndexedParams &p);
 hipError_t launch_indexed_mfma(const IndexedParams &p, hipStream_t stream);
 
 hipError_t launch_build_topk_idxs(const BuildIdxParams &p, hipStream_t stream);
+hipError_t launch_compress_pool(const CompressParams &p, int elem_type, hipStream_t stream);
 
 // Per-block attention mass of the lists (IndexedParams block-mass fields).
 hipError_t launch_block_mass_valu(const IndexedParams &p, int elem_type, hipStream_t stream);

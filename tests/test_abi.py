@@ -11,7 +11,8 @@ import re
 import pytest
 
 import sliding_window_attention_index_amd as sattn
-from sliding_window_attention_index_amd import _BlockMassArgs, _BuildIdxArgs, _IndexedArgs, _MergeArgs, _WindowArgs
+from sliding_window_attention_index_amd import (_BlockMassArgs, _BuildIdxArgs, _CompressArgs, _IndexedArgs, _MergeArgs,
+                                                 _WindowArgs)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sattn.h")
@@ -36,7 +37,7 @@ def _declared_functions():
 def test_header_functions_exported(lib):
     names = _declared_functions()
     assert set(names) == {"sattn_window_fwd", "sattn_indexed_fwd", "sattn_merge_lse", "sattn_build_topk_idxs",
-                          "sattn_block_mass", "sattn_indexed_workspace_size", "sattn_status_string", "sattn_abi_version"}
+                          "sattn_block_mass", "sattn_compress_pool", "sattn_indexed_workspace_size", "sattn_status_string", "sattn_abi_version"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -212,3 +213,34 @@ def test_block_mass_empty_is_noop(lib):
     assert lib.sattn_block_mass(ctypes.byref(_mass(batch=0, q=None, mass=None)), None) == OK
     assert lib.sattn_block_mass(ctypes.byref(_mass(topk=0, mass=None)), None) == OK
     assert lib.sattn_block_mass(None, None) == NULL_PTR
+
+
+def _comp(**kw):
+    base = dict(dtype=0, kv=FAKE, score=FAKE, ape=FAKE, out=FAKE, out_batch_stride=8192, batch=1, seq_len=32768,
+                head_dim=128, ratio=4, overlap=1)
+    base.update(kw)
+    return _CompressArgs(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=5), DTYPE),
+    (dict(overlap=2), ARG),
+    (dict(ratio=0), SHAPE),
+    (dict(batch=-1), SHAPE),
+    (dict(seq_len=-4), SHAPE),
+    (dict(head_dim=0), SHAPE),
+    (dict(head_dim=12), UNSUPPORTED),
+    (dict(out_batch_stride=8191), SHAPE),
+    (dict(kv=None), NULL_PTR),
+    (dict(ape=None), NULL_PTR),
+    (dict(out=FAKE + 4), ALIGNMENT),
+    (dict(score=FAKE + 8), ALIGNMENT),
+])
+def test_compress_pool_validation(lib, kw, status):
+    assert lib.sattn_compress_pool(ctypes.byref(_comp(**kw)), None) == status
+
+
+def test_compress_pool_empty_is_noop(lib):
+    assert lib.sattn_compress_pool(ctypes.byref(_comp(batch=0, kv=None)), None) == OK
+    assert lib.sattn_compress_pool(ctypes.byref(_comp(seq_len=3, out=None, out_batch_stride=0)), None) == OK
+    assert lib.sattn_compress_pool(None, None) == NULL_PTR
