@@ -1,4 +1,5 @@
-"""CPU oracle for top-k list construction, per-block attention mass and the compressor's gated
+"""CPU oracle for top-k list construction (window rows, synthetic indexer), per-block attention mass
+and the compressor's gated
 pooling (test infrastructure).
 
 Only the test suite, ``__graft_entry__.smoke()`` and the benchmark's
@@ -140,3 +141,38 @@ def compress_pool(kv, score, ape, *, ratio: int, overlap: bool) -> np.ndarray:
             e = np.exp(sc - sc.max(axis=0))
             out[b, w] = (e * np.stack(rows_kv)).sum(axis=0) / e.sum(axis=0)
     return out
+
+
+def indexer_lists(qr, kidx, start_pos, q_len: int, window: int, ratio: int, n_comp: int, topk: int,
+                  rows=None) -> np.ndarray:
+    """Top-k lists chosen by a synthetic indexer.
+
+    Source: DeepSeek-V4 CSA/HCA article, §2.3 (the indexer, fed the low-rank query qr, chooses
+    the compressed-region indices; window indices come first and the two parts are
+    concatenated).  Readings (the article gives neither the scoring nor the weights): compressed
+    row c is scored qr[b, t] . kidx[b, c] with a per-row index key kidx; only the rows visible
+    at the query's position (those query_list lists) are candidates; the `topk` highest scores
+    are kept, ties going to the lower row; the chosen rows are listed as window + c in
+    increasing c, then -1 up to `topk` entries.  Scores are taken in fp64.
+
+    qr [B, q_len, r], kidx [B, n_comp, r].  Returns int32 [B, q_len, window + topk], or
+    [len(rows), window + topk] for the flat query rows b * q_len + t named in `rows`.
+    """
+    qf = np.asarray(qr.float().numpy() if hasattr(qr, "float") else qr, dtype=np.float64)
+    kf = np.asarray(kidx.float().numpy() if hasattr(kidx, "float") else kidx, dtype=np.float64)
+    sp = np.asarray(start_pos, dtype=np.int64).reshape(-1)
+    B = sp.shape[0]
+    flat = range(B * q_len) if rows is None else [int(r) for r in rows]
+    out = np.full((len(flat), window + topk), -1, dtype=np.int32)
+    for i, r in enumerate(flat):
+        b, t = divmod(r, q_len)
+        full = query_list(int(sp[b]) + t, window, ratio, n_comp)
+        out[i, :window] = full[:window]
+        visible = [x - window for x in full[window:] if x >= 0]  # compressed indices c
+        if not visible:
+            continue
+        scores = kf[b, visible] @ qf[b, t]
+        order = sorted(range(len(visible)), key=lambda j: (-scores[j], visible[j]))
+        chosen = sorted(visible[j] for j in order[:topk])
+        out[i, window:window + len(chosen)] = [window + c for c in chosen]
+    return out if rows is not None else out.reshape(B, q_len, window + topk)
