@@ -8,13 +8,15 @@ attention (16 sequences, lengths U[1024, 4096], 16 query / 8 KV heads,
 head_dim 128, symmetric window 128, key-0 sinks, bf16).  The other workloads
 (causal window with null sinks, top-k prefill over a shared K=V cache, top-k
 decode with split-K and merge, the device-side top-k list builder, the
-per-block attention mass at the prefill shape, and the compressor pooling of the
-prefill sequence) are timed the same way and
-reported inside the same JSON line under "workloads".
+per-block attention mass at the prefill shape, the compressor pooling of the
+prefill sequence, and the synthetic indexer's top-k selection at the prefill
+shape) are timed the same way and reported inside the same JSON line under
+"workloads".
 
 To keep the 256 MB last-level cache (MALL) from serving a step's inputs from
 the previous step, every workload rotates between input sets whose union is
-larger than the MALL.
+larger than the MALL (the indexer's 2 MB of inputs are the exception: its
+21 MB of output lists dominate its traffic).
 
 Roofline: algorithmic bytes (each q/k/v/o element once for the window path;
 each listed cache row once per query, plus q/o/index lists, for the top-k
@@ -239,6 +241,44 @@ class CompressWorkload(Workload):
         sattn.compress_pool(kv, sc, self.ape, ratio=self.ratio, overlap=self.overlap, out=self.out)
 
 
+class IndexerWorkload(Workload):
+    """Synthetic indexer at the prefill shape: 8192 queries at positions 24576.. (the last 8192 of
+    32768 tokens), low-rank query and index keys of rank 64, 8192 compressed rows (ratio 4), window
+    128, the top 512 per query -> [1, 8192, 640] int32 lists.  Two input sets alternate."""
+
+    def __init__(self, device, name, start_pos=24576, q_len=8192, n_comp=8192, rank=64, window=128, ratio=4,
+                 topk=512, n_sets=2):
+        import torch
+
+        import workloads as W
+        super().__init__(device)
+        self.name = name
+        self.bound = "hbm"
+        self.case0 = None
+        self.sets = []
+        for s in range(n_sets):
+            qr, kidx = W.indexer_inputs(seed=s, batch=1, q_len=q_len, n_comp=n_comp, rank=rank)
+            self.sets.append((qr.to(device), kidx.to(device)))
+        self.sp = torch.tensor([start_pos], dtype=torch.int32, device=device)
+        K = window + topk
+        self.out = [torch.empty((1, q_len, K), dtype=torch.int32, device=device) for _ in range(n_sets)]
+        self.args = dict(window=window, ratio=ratio, n_comp=n_comp, topk=topk)
+        self.q_len = q_len
+        vis = [min(n_comp, (start_pos + t + 1) // ratio) for t in range(q_len)]
+        self.pairs = sum(vis)  # (query, visible compressed row) pairs scored
+        self.bytes = q_len * rank * 2 + n_comp * rank * 2 + 4 + q_len * K * 4
+        self.flops = 2 * rank * self.pairs
+        self.unit = "scored pairs/s"
+        self.config = dict(workload=name, batch=1, q_len=q_len, n_comp=n_comp, rank=rank, window=window,
+                           ratio=ratio, topk=topk, start_pos=start_pos, input_sets=n_sets)
+
+    def launch(self, i):
+        import sliding_window_attention_index_amd as sattn
+        j = i % len(self.sets)
+        qr, kidx = self.sets[j]
+        sattn.indexer_topk(qr, kidx, self.sp, self.q_len, out=self.out[j], **self.args)
+
+
 def build_workload(name, device):
     import workloads as W
     if name == "vision_window":
@@ -256,6 +296,8 @@ def build_workload(name, device):
         return BlockMassWorkload(device, name, W.sparse_prefill_case(seed=0), 64)
     if name == "compress_pool":
         return CompressWorkload(device, name)
+    if name == "indexer_topk":
+        return IndexerWorkload(device, name)
     if name == "topk_idx_build":
         return BuildIdxWorkload(device, name, [24576], 8192, 128, 4, 8192)
     raise ValueError(name)
@@ -374,7 +416,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="vision_window",
                     choices=["vision_window", "causal_window_null", "sparse_prefill", "sparse_decode",
-                             "topk_idx_build", "sparse_prefill_block_mass", "compress_pool"])
+                             "topk_idx_build", "sparse_prefill_block_mass", "compress_pool", "indexer_topk"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-extra", action="store_true", help="time only the headline workload")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -403,7 +445,7 @@ def main():
     names = [args.workload]
     if not args.no_extra:
         names += [n for n in ("vision_window", "causal_window_null", "sparse_prefill", "sparse_decode",
-                              "topk_idx_build", "sparse_prefill_block_mass", "compress_pool") if n != args.workload]
+                              "topk_idx_build", "sparse_prefill_block_mass", "compress_pool", "indexer_topk") if n != args.workload]
     results = {}
     main_wl = None
     for name in names:

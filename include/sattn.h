@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define SATTN_ABI_VERSION 4
+#define SATTN_ABI_VERSION 5
 
 typedef enum {
   SATTN_OK = 0,
@@ -314,6 +314,48 @@ typedef struct {
 } sattn_compress_args;
 
 sattn_status sattn_compress_pool(const sattn_compress_args *args, hipStream_t stream);
+
+/*
+ * Top-k lists chosen by a synthetic indexer (DeepSeek-V4 CSA/HCA article, §2.3: the indexer,
+ * fed the low-rank query qr, picks each query's compressed-region indices; the window indices
+ * come first and the two parts are concatenated).  The article fixes neither the scoring nor
+ * the weights; here:
+ *
+ *   out       [batch, q_len, window + topk] int32 (written), the idx argument of
+ *             sattn_indexed_fwd with topk' = window + topk
+ *   qr        [batch, q_len, rank] bf16: low-rank query of each token
+ *   kidx      [batch, n_comp, rank] bf16: index key of each compressed row
+ *   start_pos [batch] int32 device array: query t of batch row b is at position start_pos[b] + t
+ *   window, ratio, n_comp: as sattn_build_idx_args (the window part of a list is identical)
+ *   rank      16, 32, 64 or 128
+ *
+ * Errors: SHAPE for negative sizes or window < 1; ARG for ratio < 0, or ratio 0 with n_comp > 0;
+ * UNSUPPORTED for another rank, batch > 65535, or q_len * rank or n_comp * rank at or above 2^30;
+ * NULL_PTR / ALIGNMENT for a missing or misaligned pointer (qr and kidx 16-byte, out and
+ * start_pos 4-byte; kidx may be null when n_comp is 0).  batch or q_len 0 is a no-op.  The call
+ * is asynchronous on `stream` and allocates nothing.
+ *
+ * Entries [0, window) are the window part of sattn_build_topk_idxs.  The candidates are the
+ * compressed rows c the query sees ((c + 1) * ratio - 1 <= position, c < n_comp); each scores
+ * qr[b, t] . kidx[b, c] (fp32 accumulation of bf16 products); the min(topk, candidates) highest
+ * scores win, ties going to the lower c; entries window .. are the winners as rows window + c in
+ * increasing c, then -1.
+ */
+typedef struct {
+  int32_t *out;
+  const void *qr;
+  const void *kidx;
+  const int32_t *start_pos;
+  int32_t batch;
+  int32_t q_len;
+  int32_t rank;
+  int32_t window;
+  int32_t ratio;
+  int32_t n_comp;
+  int32_t topk;
+} sattn_indexer_args;
+
+sattn_status sattn_indexer_topk(const sattn_indexer_args *args, hipStream_t stream);
 
 sattn_status sattn_window_fwd(const sattn_window_args *args, hipStream_t stream);
 sattn_status sattn_indexed_fwd(const sattn_indexed_args *args, hipStream_t stream);

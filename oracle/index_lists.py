@@ -1,6 +1,5 @@
-"""CPU oracle for top-k list construction (window rows, synthetic indexer), per-block attention mass
-and the compressor's gated
-pooling (test infrastructure).
+"""CPU oracle for top-k list construction (window rows, synthetic indexer), per-block attention
+mass and the compressor's gated pooling (test infrastructure).
 
 Only the test suite, ``__graft_entry__.smoke()`` and the benchmark's
 ``cpu_baseline`` leg may import this module; the product path never does.

@@ -12,6 +12,7 @@ built, importing works but every call raises.
     idx = build_topk_idxs(start_pos, q_len, window=128, ratio=4, n_comp=8192)
     mass = block_mass(q, kv, idx, lse, block_keys=64)   # lse from indexed_fwd(..., return_lse=True)
     rows = compress_pool(kv_proj, score_proj, ape, ratio=4, overlap=True)
+    idx = indexer_topk(qr, kidx, start_pos, q_len, window=128, ratio=4, n_comp=8192, topk=512)
 """
 from __future__ import annotations
 
@@ -21,7 +22,7 @@ import os
 
 import torch  # loads the HIP runtime libsattn links against
 
-__all__ = ["window_fwd", "indexed_fwd", "merge_lse", "build_topk_idxs", "block_mass", "compress_pool",
+__all__ = ["window_fwd", "indexed_fwd", "merge_lse", "build_topk_idxs", "block_mass", "compress_pool", "indexer_topk",
            "indexed_workspace_size",
            "SattnError",
            "library_path", "load_library", "abi_version", "SINK_MODES"]
@@ -86,6 +87,13 @@ class _CompressArgs(ctypes.Structure):
                 ("overlap", ctypes.c_int32)]
 
 
+class _IndexerArgs(ctypes.Structure):
+    _fields_ = [("out", ctypes.c_void_p), ("qr", ctypes.c_void_p), ("kidx", ctypes.c_void_p),
+                ("start_pos", ctypes.c_void_p), ("batch", ctypes.c_int32), ("q_len", ctypes.c_int32),
+                ("rank", ctypes.c_int32), ("window", ctypes.c_int32), ("ratio", ctypes.c_int32),
+                ("n_comp", ctypes.c_int32), ("topk", ctypes.c_int32)]
+
+
 _LIB = None
 
 
@@ -112,6 +120,8 @@ def load_library(path: str | None = None):
     lib.sattn_block_mass.restype = ctypes.c_int
     lib.sattn_compress_pool.argtypes = [ctypes.POINTER(_CompressArgs), P]
     lib.sattn_compress_pool.restype = ctypes.c_int
+    lib.sattn_indexer_topk.argtypes = [ctypes.POINTER(_IndexerArgs), P]
+    lib.sattn_indexer_topk.restype = ctypes.c_int
     lib.sattn_indexed_workspace_size.argtypes = [ctypes.c_int32] * 5
     lib.sattn_indexed_workspace_size.restype = ctypes.c_size_t
     lib.sattn_status_string.argtypes = [ctypes.c_int]
@@ -363,4 +373,32 @@ def compress_pool(kv, score, ape, *, ratio: int, overlap: bool, out=None):
     st = _lib_handle().sattn_compress_pool(ctypes.byref(a), _stream(dev))
     if st != 0:
         raise SattnError(st, "sattn_compress_pool")
+    return out
+
+
+def indexer_topk(qr, kidx, start_pos, q_len: int, *, window: int, ratio: int, n_comp: int, topk: int, out=None):
+    """Top-k lists [B, q_len, window + topk] int32 chosen by the synthetic indexer (see include/sattn.h,
+    sattn_indexer_args): the window part of build_topk_idxs, then the `topk` visible compressed rows
+    with the highest qr . kidx scores as rows window + c in increasing c, then -1.
+
+    qr [B, q_len, rank] and kidx [B, n_comp, rank] bf16, start_pos int32 [B].
+    """
+    dev = qr.device
+    _check_dev("qr", qr, dev, torch.bfloat16)
+    _check_dev("kidx", kidx, dev, torch.bfloat16)
+    _check_dev("start_pos", start_pos, dev, torch.int32)
+    B, M, r = qr.shape
+    if M != q_len or tuple(kidx.shape) != (B, n_comp, r) or start_pos.shape != (B,):
+        raise ValueError("qr must be [B, q_len, r], kidx [B, n_comp, r] and start_pos [B]")
+    K = window + topk
+    if out is None:
+        out = torch.empty((B, q_len, K), dtype=torch.int32, device=dev)
+    else:
+        _check_dev("out", out, dev, torch.int32)
+        if tuple(out.shape) != (B, q_len, K):
+            raise ValueError(f"out must have shape {(B, q_len, K)}")
+    a = _IndexerArgs(_ptr(out), _ptr(qr), _ptr(kidx), _ptr(start_pos), B, q_len, r, window, ratio, n_comp, topk)
+    st = _lib_handle().sattn_indexer_topk(ctypes.byref(a), _stream(dev))
+    if st != 0:
+        raise SattnError(st, "sattn_indexer_topk")
     return out

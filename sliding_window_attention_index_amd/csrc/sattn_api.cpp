@@ -313,4 +313,34 @@ sattn_status sattn_compress_pool(const sattn_compress_args *a, hipStream_t strea
   return launch_status(sattn::launch_compress_pool(p, a->dtype == SATTN_F32 ? sattn::kF32 : sattn::kBF16, stream));
 }
 
+sattn_status sattn_indexer_topk(const sattn_indexer_args *a, hipStream_t stream) {
+  if (!a) return SATTN_ERR_NULL_PTR;
+  if (a->batch < 0 || a->q_len < 0 || a->window < 1 || a->n_comp < 0 || a->topk < 0) return SATTN_ERR_SHAPE;
+  if (a->ratio < 0 || (a->ratio == 0 && a->n_comp > 0)) return SATTN_ERR_ARG;
+  if (a->batch > 65535) return SATTN_ERR_UNSUPPORTED;  // one grid row per batch row
+  if (a->rank != 16 && a->rank != 32 && a->rank != 64 && a->rank != 128) return SATTN_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(a->window) + a->topk > INT32_MAX) return SATTN_ERR_SHAPE;
+  // 32-bit buffer offsets over one batch row's qr and index keys
+  if (static_cast<int64_t>(a->q_len) * a->rank * 2 >= (int64_t(1) << 31) ||
+      static_cast<int64_t>(a->n_comp) * a->rank * 2 >= (int64_t(1) << 31))
+    return SATTN_ERR_UNSUPPORTED;
+  if (a->batch == 0 || a->q_len == 0) return SATTN_OK;
+  if (!a->out || !a->qr || !a->start_pos || (a->n_comp > 0 && !a->kidx)) return SATTN_ERR_NULL_PTR;
+  if (!aligned4(a->out) || !aligned4(a->start_pos) || !aligned16(a->qr) || (a->kidx && !aligned16(a->kidx)))
+    return SATTN_ERR_ALIGNMENT;
+  sattn::IndexerParams p;
+  p.out = a->out;
+  p.qr = a->qr;
+  p.kidx = a->kidx;
+  p.start_pos = a->start_pos;
+  p.batch = a->batch;
+  p.q_len = a->q_len;
+  p.rank = a->rank;
+  p.window = a->window;
+  p.ratio = a->ratio;
+  p.n_comp = a->n_comp;
+  p.topk = a->topk;
+  return launch_status(sattn::launch_indexer_topk(p, stream));
+}
+
 }  // extern "C"

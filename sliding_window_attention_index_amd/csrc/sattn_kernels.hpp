@@ -52,6 +52,15 @@ struct IndexedParams {
   int block_keys, n_bins;
 };
 
+// Synthetic indexer: top-k compressed rows per query, after the window part of the list.
+struct IndexerParams {
+  int32_t *out;              // [batch, q_len, window + topk]
+  const void *qr;            // [batch, q_len, rank] bf16
+  const void *kidx;          // [batch, n_comp, rank] bf16
+  const int32_t *start_pos;  // [batch]
+  int batch, q_len, rank, window, ratio, n_comp, topk;
+};
+
 // Compressor pooling (one compressed row per complete window of `ratio` tokens).
 struct CompressParams {
   const void *kv, *score;  // [batch, seq_len, coff * head_dim]
@@ -84,6 +93,7 @@ hipError_t launch_indexed_mfma(const IndexedParams &p, hipStream_t stream);
 
 hipError_t launch_build_topk_idxs(const BuildIdxParams &p, hipStream_t stream);
 hipError_t launch_compress_pool(const CompressParams &p, int elem_type, hipStream_t stream);
+hipError_t launch_indexer_topk(const IndexerParams &p, hipStream_t stream);
 
 // Per-block attention mass of the lists (IndexedParams block-mass fields).
 hipError_t launch_block_mass_valu(const IndexedParams &p, int elem_type, hipStream_t stream);

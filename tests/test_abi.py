@@ -11,8 +11,8 @@ import re
 import pytest
 
 import sliding_window_attention_index_amd as sattn
-from sliding_window_attention_index_amd import (_BlockMassArgs, _BuildIdxArgs, _CompressArgs, _IndexedArgs, _MergeArgs,
-                                                 _WindowArgs)
+from sliding_window_attention_index_amd import (_BlockMassArgs, _BuildIdxArgs, _CompressArgs, _IndexedArgs,
+                                                 _IndexerArgs, _MergeArgs, _WindowArgs)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sattn.h")
@@ -37,7 +37,8 @@ def _declared_functions():
 def test_header_functions_exported(lib):
     names = _declared_functions()
     assert set(names) == {"sattn_window_fwd", "sattn_indexed_fwd", "sattn_merge_lse", "sattn_build_topk_idxs",
-                          "sattn_block_mass", "sattn_compress_pool", "sattn_indexed_workspace_size", "sattn_status_string", "sattn_abi_version"}
+                          "sattn_block_mass", "sattn_compress_pool", "sattn_indexer_topk",
+                          "sattn_indexed_workspace_size", "sattn_status_string", "sattn_abi_version"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -244,3 +245,36 @@ def test_compress_pool_empty_is_noop(lib):
     assert lib.sattn_compress_pool(ctypes.byref(_comp(batch=0, kv=None)), None) == OK
     assert lib.sattn_compress_pool(ctypes.byref(_comp(seq_len=3, out=None, out_batch_stride=0)), None) == OK
     assert lib.sattn_compress_pool(None, None) == NULL_PTR
+
+
+def _ixr(**kw):
+    base = dict(out=FAKE, qr=FAKE, kidx=FAKE, start_pos=FAKE, batch=1, q_len=8192, rank=64, window=128, ratio=4,
+                n_comp=8192, topk=512)
+    base.update(kw)
+    return _IndexerArgs(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(window=0), SHAPE),
+    (dict(topk=-1), SHAPE),
+    (dict(batch=-1), SHAPE),
+    (dict(ratio=-1), ARG),
+    (dict(ratio=0), ARG),
+    (dict(rank=48), UNSUPPORTED),
+    (dict(rank=256), UNSUPPORTED),
+    (dict(batch=65536), UNSUPPORTED),
+    (dict(n_comp=1 << 24, rank=64), UNSUPPORTED),
+    (dict(out=None), NULL_PTR),
+    (dict(kidx=None), NULL_PTR),
+    (dict(start_pos=None), NULL_PTR),
+    (dict(qr=FAKE + 4), ALIGNMENT),
+    (dict(out=FAKE + 2), ALIGNMENT),
+])
+def test_indexer_topk_validation(lib, kw, status):
+    assert lib.sattn_indexer_topk(ctypes.byref(_ixr(**kw)), None) == status
+
+
+def test_indexer_topk_empty_is_noop(lib):
+    assert lib.sattn_indexer_topk(ctypes.byref(_ixr(batch=0, out=None)), None) == OK
+    assert lib.sattn_indexer_topk(ctypes.byref(_ixr(q_len=0, qr=None)), None) == OK
+    assert lib.sattn_indexer_topk(None, None) == NULL_PTR

@@ -247,3 +247,19 @@ def causal_window_null(seed: int = 0, num_seqs: int = 4, seqlen: int = 8192) -> 
     """Causal sliding window of 128 keys (self included), 64/8 heads, D=64, null-logit sinks."""
     return make_window_case("causal_window_null", [seqlen] * num_seqs, 64, 8, 64, 127, 0, SINK_NULL,
                             dtype=torch.bfloat16, seed=seed)
+
+
+def indexer_inputs(seed: int, batch: int, q_len: int, n_comp: int, rank: int, integer: bool = False):
+    """Low-rank queries qr [batch, q_len, rank] and index keys kidx [batch, n_comp, rank], bf16.
+
+    N(0, 1) entries, or with integer=True small integers in [-3, 3] (every score is then an
+    integer, exact in fp32, and equal scores are common).
+    """
+    g = torch.Generator().manual_seed(seed)
+    if integer:
+        qr = torch.randint(-3, 4, (batch, q_len, rank), generator=g).to(torch.bfloat16)
+        kidx = torch.randint(-3, 4, (batch, n_comp, rank), generator=g).to(torch.bfloat16)
+    else:
+        qr = _randn(g, (batch, q_len, rank), torch.bfloat16)
+        kidx = _randn(g, (batch, n_comp, rank), torch.bfloat16)
+    return qr, kidx
