@@ -17,10 +17,10 @@
 // scores would not fit in LDS; the index keys stay in L2).
 //
 // Fast path, two score passes.  The selection needs only a monotone map of the scores, so the
-// first pass bins each score by its float bits >> 19 (sign, exponent and 4 mantissa bits: bins
-// 1/16 octave wide for positive scores) inside a window of 254 bins placed per query from the
-// root mean square of its first 32 scores (8 octaves below it, 8 above; everything lower falls
-// in bin 0, everything higher in bin 255), one LDS histogram per query.  A wave-parallel suffix
+// first pass bins each score by its float bits >> 18 (sign, exponent and 5 mantissa bits: bins
+// 1/32 octave wide for positive scores) inside a window of 256 codes placed per query from the
+// root mean square of its first 32 scores (from 2 octaves below it to 6 above; everything lower
+// falls in bin 0, everything higher in bin 255), one LDS histogram per query.  A wave-parallel suffix
 // scan finds the bin holding the k-th largest score.  The second pass sets one bit per row
 // above that bin in an LDS bitmap and appends the rows inside it (a few dozen for smooth score
 // distributions) to a per-query LDS bucket; each bucket member is then ranked exactly (score,
@@ -65,8 +65,10 @@ constexpr int kHistStride = 257;   // 256 bins, and a spare bin that absorbs inv
 constexpr int kMaxMapTiles = 256;  // bitmap capacity: 256 tiles = 8192 compressed rows
 constexpr int kMapStride = 257;    // words of one query's bitmap, one more against bank conflicts
 constexpr int kBucketCap = 128;    // rows of a query's threshold bin that the exact ranking takes
-constexpr int kCodeShift = 19;     // bin code: float bits >> 19
-constexpr int kWindowBelow = 128;  // the window starts 128 codes (8 octaves) below the estimate
+constexpr int kCodeShift = 18;        // bin code: float bits >> 18 (5 mantissa bits, 1/32 octave)
+constexpr int kWindowBelow = 64;      // the window starts 64 codes (2 octaves) below the estimate
+constexpr int kMinWindowCode = 32;    // the window's first code is a normal float's (2^-126 and up)
+constexpr int kMaxWindowCode = 7936;  // ... and its last code, first + 255, stays a positive float's
 
 // LDS accesses of the score passes that the compiler does not see.  A compiler-visible LDS access
 // would be preceded by a wait for every DMA in flight into this wave's slot (it cannot tell the
@@ -140,9 +142,9 @@ __global__ __launch_bounds__(64 * NW) void indexer_topk_kernel(IndexerParams a) 
   constexpr int D = 16 * S;                     // rank
   constexpr bool kDma = D == 64 || D == 128;    // staged through LDS (the swizzled tile layout)
   using Tile = SwizzledTile<kDma ? D : 64>;
+  __shared__ __align__(256) uint8_t ring[kDma ? NW * Tile::kBytes : 256];
   __shared__ HistOrBucket hb;
   __shared__ uint32_t gmap[32 * kMapStride];
-  __shared__ __align__(256) uint8_t ring[kDma ? NW * Tile::kBytes : 256];
   __shared__ uint32_t cnt_gt[NW][32], cnt_eq[NW][32];
   __shared__ uint32_t prefix[32], krem[32], total[32], bcount[32];
   __shared__ int32_t ecut[32];
@@ -158,7 +160,7 @@ __global__ __launch_bounds__(64 * NW) void indexer_topk_kernel(IndexerParams a) 
   const int M = a.q_len, R = a.rank, W = a.window, K = a.window + a.topk;
   const int64_t sp = a.start_pos[b];
 
-  auto visible_rows = [&](int64_t pos) -> int {
+  auto visible_rows = [&](int64_t pos) __attribute__((always_inline)) -> int {
     if (a.ratio <= 0 || pos < 0) return 0;
     const int64_t v = (pos + 1) / a.ratio;
     return static_cast<int>(v < a.n_comp ? v : a.n_comp);
@@ -187,13 +189,13 @@ __global__ __launch_bounds__(64 * NW) void indexer_topk_kernel(IndexerParams a) 
 
   // A operand of tile `tile` read straight from memory: index keys of rows 32 tile + n (rows past
   // n_comp read 0).
-  auto load_k = [&](int tile, u32x4 (&kf)[S]) {
+  auto load_k = [&](int tile, u32x4 (&kf)[S]) __attribute__((always_inline)) {
 #pragma unroll
     for (int s = 0; s < S; ++s)
       kf[s] = __builtin_amdgcn_raw_buffer_load_b128(
           krs, static_cast<uint32_t>((tile * 32 + n) * R + 8 * (h * S + s)) * 2, 0, 0);
   };
-  auto scores = [&](const u32x4 (&kf)[S]) {
+  auto scores = [&](const u32x4 (&kf)[S]) __attribute__((always_inline)) {
     f32x16 st = f32x16{};
 #pragma unroll
     for (int s = 0; s < S; ++s)
@@ -214,7 +216,8 @@ __global__ __launch_bounds__(64 * NW) void indexer_topk_kernel(IndexerParams a) 
     }
   }
   const uint32_t kaddr = slot_addr + Tile::offset(n, h * S);
-  auto issue_tile = [&](int tile) {  // rows past n_comp read zeros (the descriptor's range check)
+  // Rows past n_comp read zeros (the descriptor's range check).
+  auto issue_tile = [&](int tile) __attribute__((always_inline)) {
     if constexpr (kDma) {
       const uint32_t base = static_cast<uint32_t>(tile) * (32u * R * 2);
 #pragma unroll
@@ -223,7 +226,7 @@ __global__ __launch_bounds__(64 * NW) void indexer_topk_kernel(IndexerParams a) 
   };
 
   // f(tile, scores) over tiles [lo, hi), the next tile's keys fetched while a tile is scored.
-  auto for_tiles = [&](int lo, int hi, auto &&f) {
+  auto for_tiles = [&](int lo, int hi, auto &&f) __attribute__((always_inline)) {
     if (lo >= hi) return;
     if constexpr (kDma) {
       // One slot: wait for the tile, copy the A operand to registers, refill the slot with the
@@ -287,7 +290,7 @@ __global__ __launch_bounds__(64 * NW) void indexer_topk_kernel(IndexerParams a) 
     if (h == 0) {
       const float rms = cnt > 0 ? sqrtf(s2 / static_cast<float>(cnt)) : 0.0f;
       const int code = static_cast<int>(__float_as_uint(rms) >> kCodeShift);
-      ecut[n] = max(1, code - kWindowBelow) - 1;  // bin = code - ecut; bin 1 is the window's first code
+      ecut[n] = min(max(code - kWindowBelow, kMinWindowCode), kMaxWindowCode);  // the window's first code
     }
   }
   __syncthreads();
@@ -315,18 +318,26 @@ __global__ __launch_bounds__(64 * NW) void indexer_topk_kernel(IndexerParams a) 
 
   // ---- fast path, pass 1: histogram of window bins ----
   if (exact_path == 0) {
-    // bin = clamp(code, ec, ec + 255) - ec, so the clamped code indexes the row from hbase.
+    // bin = clamp(code, ec, ec + 255) - ec: bin 0 holds every score of code ec and below (the
+    // negative ones included), bin 255 every score of code ec + 255 and above.  The clamp is
+    // taken on the score itself, between the smallest float of code ec and the largest of code
+    // ec + 255 (both positive normal floats), and the clamped code indexes the row from hbase.
     const int ec = ecut[n];
+    const float lo_f = __uint_as_float(static_cast<uint32_t>(ec) << kCodeShift);
+    const float hi_f = __uint_as_float((static_cast<uint32_t>(ec + 255) << kCodeShift) | ((1u << kCodeShift) - 1));
     const uint32_t hbase = lds_addr(hist) + static_cast<uint32_t>(n * kHistStride - ec) * 4u;
-    auto clamped = [&](float x) { return min(max(static_cast<int>(__float_as_uint(x)) >> kCodeShift, ec), ec + 255); };
-    for_tiles(tile_lo, full_hi, [&](int, const f32x16 &st) {
+    auto clamped = [&](float x) __attribute__((always_inline)) {
+      return __float_as_uint(__builtin_amdgcn_fmed3f(x, lo_f, hi_f)) >> kCodeShift;
+    };
+    for_tiles(tile_lo, full_hi, [&](int, const f32x16 &st) __attribute__((always_inline)) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) ds_add_u32_raw(hbase + 4u * static_cast<uint32_t>(clamped(st[r])), 1u);
+      for (int r = 0; r < 16; ++r) ds_add_u32_raw(hbase + 4u * clamped(st[r]), 1u);
     });
-    for_tiles(full_hi, tile_hi, [&](int tile, const f32x16 &st) {
+    for_tiles(full_hi, tile_hi, [&](int tile, const f32x16 &st) __attribute__((always_inline)) {
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        ds_add_u32_raw(hbase + 4u * static_cast<uint32_t>(tile * 32 + cand_of(r, h) < vis ? clamped(st[r]) : ec + 256), 1u);
+        ds_add_u32_raw(hbase + 4u * (tile * 32 + cand_of(r, h) < vis ? clamped(st[r]) : static_cast<uint32_t>(ec + 256)),
+                       1u);
     });
     lds_drain();
     __syncthreads();
@@ -347,28 +358,40 @@ __global__ __launch_bounds__(64 * NW) void indexer_topk_kernel(IndexerParams a) 
 
   if (exact_path == 0) {
     // ---- fast path, pass 2: bitmap of the rows above the threshold bin, bucket of the rows in it ----
+    // For an interior bin B of this query's window (code eb = ec + B), with scores compared as
+    // signed integers of their bits: code > eb <=> bits > gt_bits, code >= eb <=> bits >= ge_bits.
+    // Lists that take every visible row use their visibility mask; empty lists choose nothing.
     const uint32_t tot = total[n];
-    // code > eb: chosen; code == eb: in the threshold bin.  Lists without a choice use the extremes.
-    const int eb = tot == 0 ? INT_MAX
-                            : (tot >= static_cast<uint32_t>(vis) ? INT_MIN : ecut[n] + static_cast<int>(prefix[n]));
+    const bool take_all = tot != 0 && tot >= static_cast<uint32_t>(vis);
+    int gt_bits = INT_MAX, ge_bits = INT_MAX;
+    if (tot != 0 && !take_all) {
+      const int eb = ecut[n] + static_cast<int>(prefix[n]);
+      ge_bits = eb << kCodeShift;
+      gt_bits = ge_bits | ((1 << kCodeShift) - 1);
+    }
     const uint32_t grow = lds_addr(gmap) + static_cast<uint32_t>(n * kMapStride) * 4u;
     const uint32_t bslots = lds_addr(bucket) + static_cast<uint32_t>(n * kBucketCap) * 8u;
-    auto mark = [&](int tile, const f32x16 &st, auto full) {
-      uint32_t g = 0, neq = 0;
+    // Bits are set at half 0's candidate positions and moved to this lane's half (4 h) at the end.
+    auto mark = [&](int tile, const f32x16 &st, auto full) __attribute__((always_inline)) {
+      uint32_t g = 0, nge = 0, vbits = 0;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int code = static_cast<int>(__float_as_uint(st[r])) >> kCodeShift;
+        const int x = static_cast<int>(__float_as_uint(st[r]));
         const bool v = decltype(full)::value || tile * 32 + cand_of(r, h) < vis;
-        g |= (v && code > eb) ? 1u << cand_of(r, h) : 0u;
-        neq += (v && code == eb) ? 1u : 0u;
+        const uint32_t bit = 1u << cand_of(r, 0);
+        vbits |= v ? bit : 0u;
+        g |= (v && x > gt_bits) ? bit : 0u;
+        nge += (v && x >= ge_bits) ? 1u : 0u;
       }
+      const uint32_t neq = take_all ? 0u : nge - static_cast<uint32_t>(__builtin_popcount(g));
+      g = (take_all ? vbits : g) << (4 * h);
       if (neq != 0) {  // this lane holds rows of its query's threshold bin: reserve, then fill
         uint32_t slot = ds_add_rtn_u32_raw(lds_addr(&bcount[n]), neq);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int code = static_cast<int>(__float_as_uint(st[r])) >> kCodeShift;
+          const int x = static_cast<int>(__float_as_uint(st[r]));
           const int c = tile * 32 + cand_of(r, h);
-          if ((decltype(full)::value || c < vis) && code == eb) {
+          if ((decltype(full)::value || c < vis) && x >= ge_bits && x <= gt_bits) {
             if (slot < kBucketCap) {
               u32x2 e;
               e[0] = __float_as_uint(st[r]);
@@ -382,28 +405,40 @@ __global__ __launch_bounds__(64 * NW) void indexer_topk_kernel(IndexerParams a) 
       g |= other_half(g);
       if (h == 0) ds_write_b32_raw(grow + 4u * static_cast<uint32_t>(tile), g);
     };
-    for_tiles(tile_lo, full_hi, [&](int tile, const f32x16 &st) { mark(tile, st, std::true_type{}); });
-    for_tiles(full_hi, tile_hi, [&](int tile, const f32x16 &st) { mark(tile, st, std::false_type{}); });
+    for_tiles(tile_lo, full_hi,
+              [&](int tile, const f32x16 &st) __attribute__((always_inline)) { mark(tile, st, std::true_type{}); });
+    for_tiles(full_hi, tile_hi,
+              [&](int tile, const f32x16 &st) __attribute__((always_inline)) { mark(tile, st, std::false_type{}); });
     lds_drain();
     __syncthreads();
 
     // Rank each bucket member against the others (higher score first, then lower row); the
-    // first krem of them are chosen.  Bucket members are positive floats with the same top 13
-    // bits, and rows are below 8192 here, so (low 19 bits of the score, 8191 - row) as one 32-bit
-    // key orders them exactly.  Lane l holds members l and l + 64; each member is broadcast to the
+    // first krem of them are chosen.  Bucket members are positive floats with the same top
+    // 32 - kCodeShift bits, and rows are below 8192 here, so (low kCodeShift bits of the score,
+    // 8191 - row) as one 32-bit key orders them exactly.  Lane l holds members l and l + 64; each member is broadcast to the
     // wave in turn.
     for (int q = wave; q < 32; q += NW) {
       const uint32_t m = min(__builtin_amdgcn_readfirstlane(bcount[q]), static_cast<uint32_t>(kBucketCap));
       if (m == 0) continue;
       const uint32_t take = krem[q];
       const uint2 *bq = bucket + q * kBucketCap;
-      auto key32 = [](uint2 v) { return ((v.x & 0x7ffffu) << 13) | (8191u - v.y); };
-      const uint2 m0 = static_cast<uint32_t>(lane) < m ? bq[lane] : make_uint2(0u, 8191u);
+      static_assert(kCodeShift + 13 <= 32 && kMaxMapTiles * 32 <= 8192, "bucket keys fit 32 bits");
+      auto key32 = [](uint2 v) __attribute__((always_inline)) {
+        return ((v.x & ((1u << kCodeShift) - 1)) << 13) | (8191u - v.y);
+      };
+      const uint2 m0 = static_cast<uint32_t>(lane) < m ? bq[lane] : make_uint2(0u, 8191u);  // key 0
       const uint32_t k0 = key32(m0);
       uint32_t r0 = 0;
       if (m <= 64) {
-        for (uint32_t f = 0; f < m; ++f) r0 += static_cast<uint32_t>(__builtin_amdgcn_readlane(k0, f)) > k0 ? 1u : 0u;
-        if (static_cast<uint32_t>(lane) < m && r0 < take) atomicOr(&gmap[q * kMapStride + (m0.y >> 5)], 1u << (m0.y & 31));
+        // 8 members at a time: lanes past m hold key 0, which ranks above no member.
+        const uint32_t m8 = (m + 7) & ~7u;
+        for (uint32_t f = 0; f < m8; f += 8) {
+#pragma unroll
+          for (uint32_t u = 0; u < 8; ++u)
+            r0 += static_cast<uint32_t>(__builtin_amdgcn_readlane(k0, f + u)) > k0 ? 1u : 0u;
+        }
+        if (static_cast<uint32_t>(lane) < m && r0 < take)
+          atomicOr(&gmap[q * kMapStride + (m0.y >> 5)], 1u << (m0.y & 31));
       } else {
         const uint2 m1 = static_cast<uint32_t>(lane) + 64 < m ? bq[lane + 64] : make_uint2(0u, 8191u);
         const uint32_t k1 = key32(m1);
@@ -418,7 +453,8 @@ __global__ __launch_bounds__(64 * NW) void indexer_topk_kernel(IndexerParams a) 
           r0 += kf > k0 ? 1u : 0u;
           r1 += kf > k1 ? 1u : 0u;
         }
-        if (static_cast<uint32_t>(lane) < m && r0 < take) atomicOr(&gmap[q * kMapStride + (m0.y >> 5)], 1u << (m0.y & 31));
+        if (static_cast<uint32_t>(lane) < m && r0 < take)
+          atomicOr(&gmap[q * kMapStride + (m0.y >> 5)], 1u << (m0.y & 31));
         if (static_cast<uint32_t>(lane) + 64 < m && r1 < take)
           atomicOr(&gmap[q * kMapStride + (m1.y >> 5)], 1u << (m1.y & 31));
       }
@@ -455,7 +491,7 @@ __global__ __launch_bounds__(64 * NW) void indexer_topk_kernel(IndexerParams a) 
       krem[threadIdx.x] = total[threadIdx.x];
     }
     // Keys of the 16 candidates this lane holds in tile `tile` (invisible ones flagged).
-    auto tile_keys = [&](int tile, uint32_t (&key)[16], uint32_t &vmask) {
+    auto tile_keys = [&](int tile, uint32_t (&key)[16], uint32_t &vmask) __attribute__((always_inline)) {
       u32x4 kf[S];
       load_k(tile, kf);
       const f32x16 st = scores(kf);
