@@ -164,3 +164,44 @@ def test_indexer_prefill_shape_sampled(dev):
     assert (np.diff(comp, axis=1) > 0).all()
     vis = (sp[0] + np.arange(M) + 1) // ratio
     assert (comp[:, -1] - win < vis).all()
+
+
+# The cases below steer the kernel's selection strategy through its inputs (the result must not
+# depend on it): the exact scores of every row decide the lists, whichever way they are found.
+
+def test_indexer_threshold_below_bin_window(dev):
+    """Top 70 % of the visible rows: the k-th score lies below the bin window placed from the scores'
+    root mean square (negative for these normal scores)."""
+    qr, kidx = W.indexer_inputs(seed=21, batch=1, q_len=40, n_comp=600, rank=64)
+    got = _run(dev, qr, kidx, [2399], 16, 4, 420).reshape(40, -1)
+    _check_valid(got, qr, kidx, [2399], 16, 4, 420, list(range(40)), "threshold below the bin window")
+
+
+def test_indexer_threshold_above_bin_window(dev):
+    """The first 32 rows' index keys are 10^4 times smaller than the rest, so the window placed from
+    their scores lies far below the k-th score."""
+    qr, kidx = W.indexer_inputs(seed=22, batch=1, q_len=40, n_comp=600, rank=64)
+    kidx[:, :32] = (kidx[:, :32].float() * 1e-4).to(torch.bfloat16)
+    got = _run(dev, qr, kidx, [2399], 16, 4, 60).reshape(40, -1)
+    _check_valid(got, qr, kidx, [2399], 16, 4, 60, list(range(40)), "threshold above the bin window")
+
+
+def test_indexer_large_tied_threshold_bin(dev):
+    """Integer scores in [-16, 16] over 600 rows, top 200: the k-th score's value is shared by 65 to
+    128 rows for most queries, which are then ordered by row."""
+    g = torch.Generator().manual_seed(25)
+    qr = torch.randint(-1, 2, (1, 40, 16), generator=g).to(torch.bfloat16)
+    kidx = torch.randint(-1, 2, (1, 600, 16), generator=g).to(torch.bfloat16)
+    got = _run(dev, qr, kidx, [2399], 16, 4, 200)
+    assert np.array_equal(got, IL.indexer_lists(qr, kidx, [2399], 40, 16, 4, 600, 200))
+
+
+def test_indexer_more_than_8192_visible_rows(dev):
+    """Queries that see 8704 compressed rows (beyond one bitmap's 8192)."""
+    qr, kidx = W.indexer_inputs(seed=26, batch=1, q_len=8, n_comp=8704, rank=64)
+    sp = [4 * 8704 - 1]
+    got = _run(dev, qr, kidx, sp, 32, 4, 300).reshape(8, -1)
+    _check_valid(got, qr, kidx, sp, 32, 4, 300, list(range(8)), "8704 visible rows")
+    qi, ki = W.indexer_inputs(seed=27, batch=1, q_len=8, n_comp=8704, rank=64, integer=True)
+    got = _run(dev, qi, ki, sp, 32, 4, 300)
+    assert np.array_equal(got, IL.indexer_lists(qi, ki, sp, 8, 32, 4, 8704, 300))
