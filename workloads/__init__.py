@@ -263,3 +263,21 @@ def indexer_inputs(seed: int, batch: int, q_len: int, n_comp: int, rank: int, in
         qr = _randn(g, (batch, q_len, rank), torch.bfloat16)
         kidx = _randn(g, (batch, n_comp, rank), torch.bfloat16)
     return qr, kidx
+
+
+def fp8_cache(seed: int, batch: int, n_rows: int, head_dim: int, rope_dims: int, scale_spread: int = 4):
+    """An fp8 KV cache: rows ~ N(0, 1) times a per-row power of two in [2^-spread, 2^spread]; the first
+    head_dim - rope_dims dims become e4m3 codes (torch's round-to-nearest float8_e4m3fn conversion)
+    against one power-of-two scale per row chosen so that the row's largest magnitude fits 448; the
+    last rope_dims dims stay bf16.  Returns (kv8 uint8 [B, N, D - rd], scale fp32 [B, N],
+    kv_rope bf16 [B, N, rd])."""
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(batch, n_rows, head_dim, generator=g)
+    x = x * torch.exp2(torch.randint(-scale_spread, scale_spread + 1, (batch, n_rows, 1), generator=g).float())
+    d8 = head_dim - rope_dims
+    nope = x[..., :d8]
+    amax = nope.abs().amax(-1).clamp_min(1e-30)
+    scale = torch.exp2(torch.ceil(torch.log2(amax / 448.0)))
+    kv8 = (nope / scale[..., None]).to(torch.float8_e4m3fn).view(torch.uint8)
+    kv_rope = x[..., d8:].to(torch.bfloat16)
+    return kv8.contiguous(), scale.float().contiguous(), kv_rope.contiguous()
