@@ -9,9 +9,9 @@ head_dim 128, symmetric window 128, key-0 sinks, bf16).  The other workloads
 (causal window with null sinks, top-k prefill over a shared K=V cache, top-k
 decode with split-K and merge, the device-side top-k list builder, the
 per-block attention mass at the prefill shape, the compressor pooling of the
-prefill sequence, and the synthetic indexer's top-k selection at the prefill
-shape) are timed the same way and reported inside the same JSON line under
-"workloads".
+prefill sequence, the synthetic indexer's top-k selection at the prefill
+shape, and the prefill and decode attention over an fp8 cache) are timed the
+same way and reported inside the same JSON line under "workloads".
 
 To keep the 256 MB last-level cache (MALL) from serving a step's inputs from
 the previous step, every workload rotates between input sets whose union is
@@ -148,6 +148,34 @@ class IndexedWorkload(Workload):
         sattn.indexed_fwd(self.qs[j], self.kv, self.idx[i % len(self.idx)], softmax_scale=c.scale, sinks=self.sinks,
                           sink_mode=["none", "key0", "null"][c.sink_mode], num_splits=c.num_splits, out=self.o[j],
                           workspace=self.workspace)
+
+
+class IndexedFp8Workload(IndexedWorkload):
+    """The indexed workloads over an fp8 cache: each row's first 64 dims as e4m3 codes times a
+    power-of-two scale, its last 64 (rotary) dims bf16 (196 bytes a row instead of 256)."""
+
+    RD = 64
+
+    def __init__(self, device, name, case, idx_sets, q_sets=1, bound="hbm"):
+        import workloads as W
+        super().__init__(device, name, case, idx_sets, q_sets=q_sets, bound=bound)
+        B, M, H, D, N, K = case.dims
+        kv8, sc, rope = W.fp8_cache(5, B, N, D, self.RD, scale_spread=0)
+        self.kv = None
+        self.kv8, self.sc, self.rope = kv8.to(device), sc.to(device), rope.to(device)
+        valid = [int(((t >= 0) & (t < N)).sum()) for t in idx_sets]
+        row_bytes = (D - self.RD) + 2 * self.RD + 4
+        self.bytes = valid[0] * row_bytes + 2 * B * M * H * D * 2 + B * M * K * 4
+        self.config.update(workload=name, kv_format=f"e4m3 dims 0..{D - self.RD - 1} x pow2 scale, bf16 rotary "
+                                                     f"dims {D - self.RD}..{D - 1}")
+
+    def launch(self, i):
+        import sliding_window_attention_index_amd as sattn
+        c = self.case0
+        j = i % len(self.qs)
+        sattn.indexed_fp8_fwd(self.qs[j], self.kv8, self.sc, self.rope, self.idx[i % len(self.idx)],
+                              softmax_scale=c.scale, sinks=self.sinks, sink_mode=["none", "key0", "null"][c.sink_mode],
+                              num_splits=c.num_splits, out=self.o[j], workspace=self.workspace)
 
 
 class BuildIdxWorkload(Workload):
@@ -292,6 +320,12 @@ def build_workload(name, device):
     if name == "sparse_decode":
         c = W.sparse_decode_case(seed=0, index_sets=16)
         return IndexedWorkload(device, name, c, c.extra["idx_sets"], q_sets=1, bound="hbm")
+    if name == "sparse_prefill_fp8":
+        c = W.sparse_prefill_case(seed=0)
+        return IndexedFp8Workload(device, name, c, [c.topk_idxs], q_sets=3, bound="mfma")
+    if name == "sparse_decode_fp8":
+        c = W.sparse_decode_case(seed=0, index_sets=16)
+        return IndexedFp8Workload(device, name, c, c.extra["idx_sets"], q_sets=1, bound="hbm")
     if name == "sparse_prefill_block_mass":
         return BlockMassWorkload(device, name, W.sparse_prefill_case(seed=0), 64)
     if name == "compress_pool":
@@ -416,7 +450,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="vision_window",
                     choices=["vision_window", "causal_window_null", "sparse_prefill", "sparse_decode",
-                             "topk_idx_build", "sparse_prefill_block_mass", "compress_pool", "indexer_topk"])
+                             "topk_idx_build", "sparse_prefill_block_mass", "compress_pool", "indexer_topk",
+                             "sparse_prefill_fp8", "sparse_decode_fp8"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-extra", action="store_true", help="time only the headline workload")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -445,7 +480,8 @@ def main():
     names = [args.workload]
     if not args.no_extra:
         names += [n for n in ("vision_window", "causal_window_null", "sparse_prefill", "sparse_decode",
-                              "topk_idx_build", "sparse_prefill_block_mass", "compress_pool", "indexer_topk") if n != args.workload]
+                              "topk_idx_build", "sparse_prefill_block_mass", "compress_pool", "indexer_topk",
+                             "sparse_prefill_fp8", "sparse_decode_fp8") if n != args.workload]
     results = {}
     main_wl = None
     for name in names:

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define SATTN_ABI_VERSION 5
+#define SATTN_ABI_VERSION 6
 
 typedef enum {
   SATTN_OK = 0,
@@ -356,6 +356,50 @@ typedef struct {
 } sattn_indexer_args;
 
 sattn_status sattn_indexer_topk(const sattn_indexer_args *args, hipStream_t stream);
+
+/*
+ * Top-k index-gathered attention (as sattn_indexed_fwd) over an fp8 cache (DeepSeek-V4 CSA/HCA
+ * article, §5.3: the compressed kv is quantised with the dims that carry no rotary embedding in
+ * fp8 and the rotary dims at higher precision; §4.1-§4.4: the gathered attention).  The article
+ * fixes no layout; the one taken here:
+ *
+ *   q, topk_idxs, o, lse, softmax_scale, sinks, sink_mode, num_splits, workspace: as
+ *             sattn_indexed_args with dtype bf16 (the workspace size is the same)
+ *   kv_fp8    [batch, kv_len, head_dim - rope_dims] uint8: e4m3 codes (OCP "fn": bias 7, no
+ *             infinities; S.1111.111 is NaN) of the first head_dim - rope_dims dims of each row
+ *   kv_scale  [batch, kv_len] fp32: one power-of-two scale per row (other values act as the
+ *             power of two of their exponent); row value = e4m3(code) * scale
+ *   kv_rope   [batch, kv_len, rope_dims] bf16: the last rope_dims dims of each row (NULL when
+ *             rope_dims is 0)
+ *   head_dim  128; rope_dims 0 or 64; num_heads a multiple of 32; softmax_scale > 0
+ *
+ * Errors as sattn_indexed_fwd; other head_dim / rope_dims / num_heads values or scale <= 0 give
+ * UNSUPPORTED.  kv_fp8, kv_rope and q 16-byte aligned; kv_scale 4-byte aligned.
+ */
+typedef struct {
+  const void *q;
+  const uint8_t *kv_fp8;
+  const float *kv_scale;
+  const void *kv_rope;
+  const int32_t *topk_idxs;
+  void *o;
+  float *lse;
+  int32_t batch;
+  int32_t q_len;
+  int32_t num_heads;
+  int32_t head_dim;
+  int32_t rope_dims;
+  int32_t kv_len;
+  int32_t topk;
+  float softmax_scale;
+  const float *sinks;
+  sattn_sink_mode sink_mode;
+  int32_t num_splits;
+  void *workspace;
+  size_t workspace_bytes;
+} sattn_indexed_fp8_args;
+
+sattn_status sattn_indexed_fp8_fwd(const sattn_indexed_fp8_args *args, hipStream_t stream);
 
 sattn_status sattn_window_fwd(const sattn_window_args *args, hipStream_t stream);
 sattn_status sattn_indexed_fwd(const sattn_indexed_args *args, hipStream_t stream);

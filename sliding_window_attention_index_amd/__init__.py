@@ -22,7 +22,7 @@ import os
 
 import torch  # loads the HIP runtime libsattn links against
 
-__all__ = ["window_fwd", "indexed_fwd", "merge_lse", "build_topk_idxs", "block_mass", "compress_pool", "indexer_topk",
+__all__ = ["window_fwd", "indexed_fwd", "indexed_fp8_fwd", "merge_lse", "build_topk_idxs", "block_mass", "compress_pool", "indexer_topk",
            "indexed_workspace_size",
            "SattnError",
            "library_path", "load_library", "abi_version", "SINK_MODES"]
@@ -56,6 +56,16 @@ class _IndexedArgs(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("kv_len", ctypes.c_int32), ("topk", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float), ("sinks", ctypes.c_void_p), ("sink_mode", ctypes.c_int),
                 ("num_splits", ctypes.c_int32), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class _IndexedFp8Args(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("kv_fp8", ctypes.c_void_p), ("kv_scale", ctypes.c_void_p),
+                ("kv_rope", ctypes.c_void_p), ("topk_idxs", ctypes.c_void_p), ("o", ctypes.c_void_p),
+                ("lse", ctypes.c_void_p), ("batch", ctypes.c_int32), ("q_len", ctypes.c_int32),
+                ("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("rope_dims", ctypes.c_int32),
+                ("kv_len", ctypes.c_int32), ("topk", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+                ("sinks", ctypes.c_void_p), ("sink_mode", ctypes.c_int), ("num_splits", ctypes.c_int32),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
 
 
 class _MergeArgs(ctypes.Structure):
@@ -120,6 +130,8 @@ def load_library(path: str | None = None):
     lib.sattn_block_mass.restype = ctypes.c_int
     lib.sattn_compress_pool.argtypes = [ctypes.POINTER(_CompressArgs), P]
     lib.sattn_compress_pool.restype = ctypes.c_int
+    lib.sattn_indexed_fp8_fwd.argtypes = [ctypes.POINTER(_IndexedFp8Args), P]
+    lib.sattn_indexed_fp8_fwd.restype = ctypes.c_int
     lib.sattn_indexer_topk.argtypes = [ctypes.POINTER(_IndexerArgs), P]
     lib.sattn_indexer_topk.restype = ctypes.c_int
     lib.sattn_indexed_workspace_size.argtypes = [ctypes.c_int32] * 5
@@ -242,6 +254,50 @@ def indexed_fwd(q, kv, topk_idxs, *, softmax_scale: float | None = None, sinks=N
     st = _lib_handle().sattn_indexed_fwd(ctypes.byref(a), _stream(dev))
     if st != 0:
         raise SattnError(st, "sattn_indexed_fwd")
+    return (o, lse) if return_lse else o
+
+
+def indexed_fp8_fwd(q, kv_fp8, kv_scale, kv_rope, topk_idxs, *, softmax_scale: float | None = None, sinks=None,
+                    sink_mode="none", num_splits: int = 1, out=None, return_lse: bool = False, workspace=None):
+    """Top-k gathered attention over an fp8 cache (see include/sattn.h, sattn_indexed_fp8_args).
+
+    q bf16 [B,M,H,128]; kv_fp8 uint8 [B,N,128-rd] e4m3 codes; kv_scale fp32 [B,N] powers of two;
+    kv_rope bf16 [B,N,rd] or None (rd = 0); topk_idxs int32 [B,M,K] (-1 = unused).
+    """
+    dev = q.device
+    _check_dev("q", q, dev, torch.bfloat16)
+    _check_dev("kv_fp8", kv_fp8, dev, torch.uint8)
+    _check_dev("kv_scale", kv_scale, dev, torch.float32)
+    _check_dev("topk_idxs", topk_idxs, dev, torch.int32)
+    B, M, H, D = q.shape
+    N = kv_fp8.shape[1]
+    rd = 0 if kv_rope is None else kv_rope.shape[2]
+    if kv_rope is not None:
+        _check_dev("kv_rope", kv_rope, dev, torch.bfloat16)
+        if kv_rope.shape[:2] != (B, N):
+            raise ValueError("kv_rope must be [B, N, rope_dims]")
+    K = topk_idxs.shape[2]
+    if kv_fp8.shape != (B, N, D - rd) or kv_scale.shape != (B, N) or topk_idxs.shape[:2] != (B, M):
+        raise ValueError("kv_fp8 must be [B, N, D - rope_dims], kv_scale [B, N] and topk_idxs [B, M, K]")
+    mode = _sink_mode(sink_mode, sinks)
+    if sinks is not None:
+        _check_dev("sinks", sinks, dev, torch.float32)
+    o = torch.empty_like(q) if out is None else out
+    _check_dev("out", o, dev, torch.bfloat16)
+    lse = torch.empty((B, M, H), dtype=torch.float32, device=dev) if return_lse else None
+    ws_bytes = indexed_workspace_size(B, M, H, D, num_splits)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _check_dev("workspace", workspace, dev)
+    a = _IndexedFp8Args(_ptr(q), _ptr(kv_fp8), _ptr(kv_scale), _ptr(kv_rope) if rd else None, _ptr(topk_idxs),
+                        _ptr(o), _ptr(lse), B, M, H, D, rd, N, K,
+                        float(1.0 / math.sqrt(D) if softmax_scale is None else softmax_scale),
+                        _ptr(sinks) if mode else None, mode, int(num_splits), _ptr(workspace),
+                        0 if workspace is None else workspace.numel() * workspace.element_size())
+    st = _lib_handle().sattn_indexed_fp8_fwd(ctypes.byref(a), _stream(dev))
+    if st != 0:
+        raise SattnError(st, "sattn_indexed_fp8_fwd")
     return (o, lse) if return_lse else o
 
 

@@ -22,13 +22,14 @@ LIB = os.path.join(PKG, "libsattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["sattn_api.cpp", "valu_fwd.hip", "indexed_mfma.hip", "window_mfma.hip", "index_build.hip", "compress.hip",
-           "indexer.hip"]
+SOURCES = ["sattn_api.cpp", "valu_fwd.hip", "indexed_mfma.hip", "indexed_fp8.hip", "window_mfma.hip", "index_build.hip",
+           "compress.hip", "indexer.hip"]
 HEADERS = ["sattn_device.hpp", "sattn_kernels.hpp", "softmax_block.hpp", "lds_tile.hpp"]
 # MFMA kernels keep their accumulators in VGPRs: the online-softmax rescale is a VALU
 # multiply, which cannot read AGPRs and would otherwise copy the accumulator every block.
 EXTRA_FLAGS = {
     "indexed_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "indexed_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "window_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 

@@ -1,0 +1,386 @@
+// Top-k index-gathered attention over an fp8 K=V cache (bf16 queries and outputs, MFMA).
+//
+// Problem: as the bf16 indexed kernel (DeepSeek-V4 CSA/HCA article, §4.1-§4.4: one shared cache
+// row per token is the key and the value of every head, -1 marks unused list entries), over a
+// cache quantised as the article's §5.3 describes for the compressed kv: the dims without rotary
+// embedding in fp8, the rotary dims at higher precision.  Layout here (the article fixes none):
+// a row of 128 dims holds its first 128 - RD dims as e4m3 codes (OCP fn) times one power-of-two
+// fp32 scale per row, and its last RD dims (0 or 64) as bf16.
+//
+// gfx950 mapping: one wave64 per task (a query, 32 of its heads, one slice of its list), four
+// independent waves per workgroup, as in the bf16 kernel.  Per 32-row block the wave DMAs into one
+// of NT wave-private LDS slots: the rows' fp8 bytes (row-major), their scales and, when RD = 64,
+// their bf16 rotary dims straight into a swizzled 32 x 64 tile.  When the block's DMAs have landed
+// the wave converts its fp8 bytes to bf16 with v_cvt_scalef32_pk_bf16_fp8 (an fp8 value times a
+// power of two is exact in bf16) into swizzled 32 x 64 tiles, so that the product code of the
+// bf16 kernel runs unchanged on two 64-dim tiles: with the MFMA step mapping of logical chunk
+// h*S + s, lanes of half 0 read only dims 0..63 and lanes of half 1 only dims 64..127.  The fp8
+// rows halve (RD = 0) or cut by a quarter (RD = 64) the bytes gathered per row.
+#include "lds_tile.hpp"
+#include "sattn_device.hpp"
+#include "sattn_kernels.hpp"
+#include "softmax_block.hpp"
+
+namespace sattn {
+namespace {
+
+constexpr int kBlockKeys = 32;
+constexpr int kIdxCap = 512;  // list entries staged per wave at a time
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// LDS read of one dword the compiler does not see (it would otherwise wait for every DMA in
+// flight before reading LDS); the result is tied to an lgkmcnt(0) wait.
+__device__ __forceinline__ int ds_read_i32(uint32_t addr) {
+  int r;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(r) : "v"(addr));
+  return r;
+}
+
+// LDS read of one dword the compiler does not see, without a wait (lgkm_fence orders it).
+__device__ __forceinline__ uint32_t ds_read_b32_raw(uint32_t addr) {
+  uint32_t r;
+  asm volatile("ds_read_b32 %0, %1" : "=v"(r) : "v"(addr));
+  return r;
+}
+
+// One 4-byte DMA per lane from rsrc + voffset into lds (+4 * lane).
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t rsrc, void *lds, uint32_t voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t *)(lds), 4, voffset, 0, 0, 0);
+}
+
+// Eight e4m3 codes (two dwords) times a power-of-two scale -> eight bf16 (four dwords).
+__device__ __forceinline__ u32x4 fp8x8_to_bf16(uint32_t w0, uint32_t w1, float scale) {
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, scale, false));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, scale, true));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, scale, false));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, scale, true));
+  return r;
+}
+
+template <int RD, int NT>
+__global__ __launch_bounds__(256) void indexed_fp8_mfma(IndexedParams p) {
+  constexpr int D = 128;
+  constexpr int S = D / 16;   // MFMA steps over head_dim
+  constexpr int DB = D / 32;  // 32-wide blocks of output dims
+  using T64 = SwizzledTile<64>;
+  constexpr int D8 = D - RD;                          // fp8 bytes per row
+  constexpr int kF8Bytes = kBlockKeys * D8;           // a block's fp8 bytes
+  constexpr int kRopeBytes = RD ? T64::kBytes : 0;    // a block's rotary tile
+  constexpr int kSlotBytes = kRopeBytes + kF8Bytes + 256;  // + scales (64 lanes x 4 bytes)
+  constexpr int kF8Dma = kF8Bytes / 1024;
+  constexpr int kRopeDma = RD ? T64::kDmaPerTile : 0;
+  constexpr int kDpb = kF8Dma + kRopeDma + 1;         // DMA instructions per block
+  constexpr int kConvTiles = RD ? 1 : 2;              // 64-dim tiles converted from fp8
+  static_assert(RD == 0 || RD == 64, "rotary dims");
+  static_assert((NT & (NT - 1)) == 0 && NT >= 2 && NT <= 4, "ring size");
+  static_assert(kSlotBytes % 256 == 0, "slot bases keep bits 4..7 clear");
+  __shared__ __attribute__((aligned(1024))) char ring[4][NT * kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) char conv[4][kConvTiles * T64::kBytes];
+  __shared__ __attribute__((aligned(16))) int32_t lists[4][kIdxCap];
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = lane_id();
+  const int h = lane >> 5;   // half of the wave: which half of head_dim / which key quads
+  const int n = lane & 31;   // key row (A operand) / head (B operand and outputs)
+  const int H = p.num_heads, N = p.kv_len, K = p.topk;
+  const int n_hg = H / 32;
+  const int64_t BM = static_cast<int64_t>(p.batch) * p.q_len;
+  const int64_t task = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  if (task >= BM * n_hg * p.num_parts) return;
+  const int hg = static_cast<int>(task % n_hg);
+  const int64_t rest = task / n_hg;
+  const int64_t bt = rest % BM;
+  const int part = static_cast<int>(rest / BM);
+  const int64_t b = bt / p.q_len;
+  const int head0 = hg * 32;
+  const bool partial = p.num_parts > 1;
+  const bool key0 = p.sink_mode == kSinkKey0;
+  const bool null_sink = !partial && p.sink_mode == kSinkNull;
+
+  // B operand of S^T: q[bt, head0 + n, h*D/2 + 8s .. +8] (logical chunk h*S + s of the row).
+  bf16x8 qf[S];
+  {
+    const __bf16 *qrow = static_cast<const __bf16 *>(p.q) + (bt * H + head0 + n) * D + h * (D / 2);
+#pragma unroll
+    for (int s = 0; s < S; ++s) qf[s] = *reinterpret_cast<const bf16x8 *>(qrow + s * 8);
+  }
+  const float c = p.scale_log2;  // > 0 on this path
+  const float sink_raw = p.sinks ? p.sinks[head0 + n] * kLog2e / c : 0.0f;  // raw logit units
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+  RowSoftmax rs;
+  rs.m = null_sink ? sink_raw : kNegInf;
+  rs.l = (null_sink && h == 0) ? 1.0f : 0.0f;  // the pair of lanes sharing a head splits l
+
+  const int kb = part * p.part_len;
+  const int ke = min(K, kb + p.part_len);
+  // This batch row's cache parts and this query's list through bounds-checked buffer resources.
+  const __amdgpu_buffer_rsrc_t f8rs = make_rsrc(static_cast<const uint8_t *>(p.kv) + b * static_cast<int64_t>(N) * D8,
+                                                static_cast<uint32_t>(N) * D8);
+  const __amdgpu_buffer_rsrc_t scrs = make_rsrc(p.kv_scale + b * static_cast<int64_t>(N), static_cast<uint32_t>(N) * 4u);
+  const __amdgpu_buffer_rsrc_t rprs =
+      make_rsrc(RD ? static_cast<const __bf16 *>(p.kv_rope) + b * static_cast<int64_t>(N) * RD : p.kv,
+                RD ? static_cast<uint32_t>(N) * RD * 2u : 0u);
+  const __amdgpu_buffer_rsrc_t lrs = make_rsrc(p.idx + bt * K, static_cast<uint32_t>(K) * 4u);
+  char *const wring = ring[wave];
+  const uint32_t ring_addr = lds_addr(wring);
+  const uint32_t conv_addr = lds_addr(conv[wave]);
+  int32_t *list = lists[wave];
+  const uint32_t list_addr = lds_addr(list);
+
+  // Slot layout: [rotary tile (RD = 64)][fp8 bytes, row-major][scales].  Tile row r holds list
+  // entry r of the block.  DMA instruction u of the fp8 bytes covers rows 1024 u / D8 ..; lane l
+  // fetches 16 bytes of row (1024 u + 16 l) / D8.
+  // The entries a lane needs for one block: the rows of its fp8 pieces, of its rotary pieces and
+  // (lanes 0..31) of its scale, read together and waited for once.
+  constexpr int kF8LanesPerRow = D8 / 16;
+  constexpr int kReads = kF8Dma + kRopeDma + 1;
+  auto issue_block = [&](int j) {
+    char *slot = wring + (j & (NT - 1)) * kSlotBytes;
+    const uint32_t lbase = list_addr + static_cast<uint32_t>(j * kBlockKeys) * 4u;
+    uint32_t xs[kReads];
+#pragma unroll
+    for (int u = 0; u < kF8Dma; ++u) xs[u] = ds_read_b32_raw(lbase + ((1024 * u + 16 * lane) / D8) * 4);
+#pragma unroll
+    for (int u = 0; u < kRopeDma; ++u) {
+      int row, chunk;
+      T64::dma_source(u, lane, row, chunk);
+      xs[kF8Dma + u] = ds_read_b32_raw(lbase + row * 4);
+    }
+    xs[kReads - 1] = ds_read_b32_raw(lbase + (lane & (kBlockKeys - 1)) * 4);
+    lgkm_fence<0>(xs);
+    auto valid = [&](uint32_t x) { return static_cast<int>(x) >= 0 && static_cast<int>(x) < N; };
+#pragma unroll
+    for (int u = 0; u < kF8Dma; ++u) {
+      const uint32_t off = valid(xs[u]) ? xs[u] * D8 + (lane % kF8LanesPerRow) * 16 : 0xfffff000u;
+      dma16(f8rs, slot + kRopeBytes + u * 1024, off);
+    }
+#pragma unroll
+    for (int u = 0; u < kRopeDma; ++u) {
+      int row, chunk;
+      T64::dma_source(u, lane, row, chunk);
+      const uint32_t x = xs[kF8Dma + u];
+      dma16(rprs, slot + u * 1024, valid(x) ? x * (RD * 2) + chunk * 16 : 0xfffff000u);
+    }
+    {
+      const uint32_t x = xs[kReads - 1];
+      dma4(scrs, slot + kRopeBytes + kF8Bytes, lane < kBlockKeys && valid(x) ? x * 4u : 0xfffff000u);
+    }
+  };
+
+  // fp8 -> bf16: lane (r = lane / 2, g = lane % 2) converts half g of row r's fp8 bytes into the
+  // 64-dim tile(s): RD = 0, 64 bytes into tile g (dims 64 g ..); RD = 64, 32 bytes into chunks
+  // 4 g .. 4 g + 3 of the one converted tile.
+  const int cr = lane >> 1, cg = lane & 1;
+  constexpr int kConvBytesPerLane = D8 / 2;
+  auto convert_block = [&](int slot_i) {
+    const uint32_t sa = ring_addr + slot_i * kSlotBytes;
+    const uint32_t src = sa + kRopeBytes + cr * D8 + cg * kConvBytesPerLane;
+    u32x4 raw[kConvBytesPerLane / 16];
+#pragma unroll
+    for (int i = 0; i < kConvBytesPerLane / 16; ++i) raw[i] = ds_read_b128<0>(src + 16 * i);
+    int sc_bits[1];
+    sc_bits[0] = ds_read_i32(sa + kRopeBytes + kF8Bytes + cr * 4);
+    lgkm_fence<0>(raw);
+    const float scale = __int_as_float(sc_bits[0]);
+    const uint32_t tile = conv_addr + (RD ? 0 : cg * T64::kBytes);
+    const int chunk0 = RD ? 4 * cg : 0;
+#pragma unroll
+    for (int i = 0; i < kConvBytesPerLane / 16; ++i) {
+      const u32x4 lo = fp8x8_to_bf16(raw[i][0], raw[i][1], scale);
+      const u32x4 hi = fp8x8_to_bf16(raw[i][2], raw[i][3], scale);
+      ds_write_b128<0>(tile + T64::offset(cr, chunk0 + 2 * i), lo);
+      ds_write_b128<0>(tile + T64::offset(cr, chunk0 + 2 * i + 1), hi);
+    }
+  };
+
+  // LDS operand addresses (tile bases have bits 4..7 clear).  K rows: lane (n, h) reads logical
+  // chunk s of row n of its half's tile at kbase ^ 16 s; V^T quads of dims 32 db .. at the D = 64
+  // tile addresses of the bf16 kernel, in the tile of dims 64 (db / 2) ...
+  const uint32_t tileA = conv_addr;
+  auto tileB = [&](int slot_i) -> uint32_t {
+    return RD ? ring_addr + slot_i * kSlotBytes : conv_addr + T64::kBytes;
+  };
+  const uint32_t koff = T64::offset(n, 0);
+  uint32_t voff;
+  {
+    const int g16 = lane >> 4, i16 = lane & 15;
+    const int c2 = 2 * (g16 & 1) + ((i16 & 3) >> 1);
+    voff = T64::offset(4 * h + (i16 >> 2), c2) + (i16 & 1) * 8;
+  }
+  constexpr int kRow8 = 8 * T64::kRowBytes;
+
+  auto compute = [&](int slot_i, uint32_t vmask, uint32_t zmask) {
+    const uint32_t tb = tileB(slot_i);
+    uint32_t kb_ = (h == 0 ? tileA : tb) + koff;
+    asm volatile("" : "+v"(kb_));
+    u32x4 kf[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) kf[s] = ds_read_b128<0>(kb_ ^ (16u * s));
+    lgkm_fence<0>(kf);
+    f32x16 st = f32x16{};
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[s]), qf[s], st, 0, 0, 0);
+    uint32_t vbA = tileA + voff, vbB = tb + voff;
+    asm volatile("" : "+v"(vbA), "+v"(vbB));
+    u32x2 vr[4 * DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const uint32_t vb = db < 2 ? vbA : vbB;
+      const uint32_t dx = 64u * (db & 1);
+      vr[db * 2] = ds_read_tr_b16<0>(vb ^ dx);
+      vr[db * 2 + 1] = ds_read_tr_b16<kRow8>(vb ^ (dx + 16u));
+      vr[2 * DB + db * 2] = ds_read_tr_b16<2 * kRow8>(vb ^ dx);
+      vr[2 * DB + db * 2 + 1] = ds_read_tr_b16<3 * kRow8>(vb ^ (dx + 16u));
+    }
+    // Accumulator element r of lane (n, h) is key 8*(r/4) + 4h + r%4 of head n.
+    if (zmask) bias_block(st, zmask, h, sink_raw);
+    if (vmask != 0xffffffffu) mask_block(st, vmask, h);
+    float alpha;
+    if (softmax_need_rescale(rs, block_max(st), c, alpha)) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+    }
+    bf16x8 pb[2];
+    softmax_probs(st, rs, c, pb);
+    lgkm_fence<0>(vr);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const u32x2 ra = vr[(tt * DB + db) * 2], rb = vr[(tt * DB + db) * 2 + 1];
+        const u32x4 av = {ra[0], ra[1], rb[0], rb[1]};
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pb[tt], acc[db], 0, 0, 0);
+      }
+  };
+
+  for (int c0 = kb; c0 < ke; c0 += kIdxCap) {
+    const int cend = min(ke, c0 + kIdxCap);
+    const int nblk = (cend - c0 + kBlockKeys - 1) / kBlockKeys;
+    asm volatile("" ::: "memory");  // the previous chunk's list reads (inline asm) stay before these stores
+    // Stage the chunk's entries (-1 past its end).  Every DMA of the previous chunk has been
+    // waited for, so nothing reads or fills LDS meanwhile.
+    {
+      constexpr int kLoads = kIdxCap / 256;
+      u32x4 v[kLoads];
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i)
+        v[i] = (256 * i < nblk * kBlockKeys)
+                   ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   lrs, static_cast<uint32_t>(c0 + 256 * i + 4 * lane) * 4u, 0, 0))
+                   : u32x4{};
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) {
+        const int j = 256 * i + 4 * lane;
+        if (j < nblk * kBlockKeys) {
+          u32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = c0 + j + e < cend ? v[i][e] : 0xffffffffu;
+          *reinterpret_cast<u32x4 *>(list + j) = w;
+        }
+      }
+    }
+    wave_lds_sync();
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+      if (j < nblk) issue_block(j);
+    for (int j = 0; j < nblk; ++j) {
+      // This wave's DMAs younger than block j's: those of the next min(NT - 1, nblk - 1 - j) blocks.
+      const int younger = min(NT - 1, nblk - 1 - j);
+      if (younger == 3) wait_vmcnt<3 * kDpb>();
+      else if (younger == 2) wait_vmcnt<2 * kDpb>();
+      else if (younger == 1) wait_vmcnt<kDpb>();
+      else wait_vmcnt<0>();
+      const int x = ds_read_i32(list_addr + (j * kBlockKeys + n) * 4);  // tile row n's entry
+      const bool valid = x >= 0 && x < N;
+      const uint32_t vmask = static_cast<uint32_t>(__ballot(valid));
+      const uint32_t zmask = key0 ? static_cast<uint32_t>(__ballot(valid && x == 0)) : 0u;
+      if (vmask != 0u) {
+        convert_block(j & (NT - 1));
+        compute(j & (NT - 1), vmask, zmask);
+      }
+      if (j + NT < nblk) issue_block(j + NT);  // the slot's reads are done (lgkm fences above)
+    }
+  }
+
+  // Epilogue: o = acc / l, lse = ln(2) * (m + log2 l).  Lane (n, h) holds dims 32db + 8j + 4h + {0..3}
+  // of head n.  Each 32-dim block goes through the wave's converted tile area as scaled fp32
+  // (16-byte chunk q of row r at q ^ (r & 7)) and comes back as 8 consecutive dims per lane.
+  const float l_tot = halves_sum(rs.l);
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  const float lse_v = l_tot > 0.0f ? (rs.m * c + log2f(l_tot)) * kLn2 : kNegInf;
+  const int64_t row0 = partial ? (static_cast<int64_t>(part) * BM + bt) * H + head0 : bt * H + head0;
+  const int rl = lane >> 2, q4 = lane & 3;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x4 w = {__float_as_uint(acc[db][4 * j] * inv), __float_as_uint(acc[db][4 * j + 1] * inv),
+                       __float_as_uint(acc[db][4 * j + 2] * inv), __float_as_uint(acc[db][4 * j + 3] * inv)};
+      ds_write_b128<0>(conv_addr + n * 128 + (((2 * j + h) ^ (n & 7)) << 4), w);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = 16 * i + rl;  // head head0 + r
+      u32x4 x[2];
+      x[0] = ds_read_b128<0>(conv_addr + r * 128 + (((2 * q4) ^ (r & 7)) << 4));
+      x[1] = ds_read_b128<0>(conv_addr + r * 128 + (((2 * q4 + 1) ^ (r & 7)) << 4));
+      lgkm_fence<0>(x);
+      const int64_t e0 = (row0 + r) * D + 32 * db + 8 * q4;
+      if (partial) {
+        *reinterpret_cast<u32x4 *>(p.part_o + e0) = x[0];
+        *reinterpret_cast<u32x4 *>(p.part_o + e0 + 4) = x[1];
+      } else {
+        const bf16x8 v = {static_cast<__bf16>(__uint_as_float(x[0][0])), static_cast<__bf16>(__uint_as_float(x[0][1])),
+                          static_cast<__bf16>(__uint_as_float(x[0][2])), static_cast<__bf16>(__uint_as_float(x[0][3])),
+                          static_cast<__bf16>(__uint_as_float(x[1][0])), static_cast<__bf16>(__uint_as_float(x[1][1])),
+                          static_cast<__bf16>(__uint_as_float(x[1][2])), static_cast<__bf16>(__uint_as_float(x[1][3]))};
+        *reinterpret_cast<bf16x8 *>(static_cast<__bf16 *>(p.o) + e0) = v;
+      }
+    }
+  }
+  if (h == 0) {
+    if (partial) p.part_lse[row0 + n] = lse_v;
+    else if (p.lse) p.lse[row0 + n] = lse_v;
+  }
+}
+
+template <int RD, int NT>
+hipError_t launch(const IndexedParams &p, hipStream_t stream) {
+  const int n_hg = p.num_heads / 32;
+  const int64_t tasks = static_cast<int64_t>(p.batch) * p.q_len * n_hg * p.num_parts;
+  const int64_t blocks = (tasks + 3) / 4;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((indexed_fp8_mfma<RD, NT>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool indexed_fp8_supported(const IndexedParams &p) {
+  // One batch row's cache parts and list are addressed with 32-bit buffer offsets.
+  const int64_t row_bytes = (p.head_dim - p.rope_dims) + 2 * p.rope_dims;
+  return p.scale_log2 > 0.0f && p.head_dim == 128 && (p.rope_dims == 0 || p.rope_dims == 64) &&
+         p.num_heads % 32 == 0 && static_cast<int64_t>(p.kv_len) * row_bytes < (int64_t(1) << 31) - 4096 &&
+         static_cast<int64_t>(p.topk) * 4 < (int64_t(1) << 31);
+}
+
+hipError_t launch_indexed_fp8(const IndexedParams &p, hipStream_t stream) {
+  // Few tasks (decode-like): one workgroup per CU anyway, so each wave keeps four blocks in flight.
+  const int64_t tasks = static_cast<int64_t>(p.batch) * p.q_len * (p.num_heads / 32) * p.num_parts;
+  const bool deep = tasks < 4096;
+  if (p.rope_dims == 64) return deep ? launch<64, 4>(p, stream) : launch<64, 2>(p, stream);
+  return deep ? launch<0, 4>(p, stream) : launch<0, 2>(p, stream);
+}
+
+}  // namespace sattn

@@ -343,4 +343,75 @@ sattn_status sattn_indexer_topk(const sattn_indexer_args *a, hipStream_t stream)
   return launch_status(sattn::launch_indexer_topk(p, stream));
 }
 
+sattn_status sattn_indexed_fp8_fwd(const sattn_indexed_fp8_args *a, hipStream_t stream) {
+  if (!a) return SATTN_ERR_NULL_PTR;
+  if (!valid_sink(a->sink_mode)) return SATTN_ERR_ARG;
+  if (a->batch < 0 || a->q_len < 0 || a->num_heads <= 0 || a->kv_len < 0 || a->topk < 0 || a->head_dim <= 0 ||
+      a->rope_dims < 0 || a->rope_dims > a->head_dim)
+    return SATTN_ERR_SHAPE;
+  if (!isfinite(a->softmax_scale)) return SATTN_ERR_ARG;
+  if (a->num_splits < 1 || a->num_splits > (a->topk > 0 ? a->topk : 1)) return SATTN_ERR_ARG;
+  const int64_t rows = static_cast<int64_t>(a->batch) * a->q_len;
+  if (rows == 0) return SATTN_OK;
+  if (rows > INT32_MAX) return SATTN_ERR_UNSUPPORTED;
+  if (!a->q || !a->o || (a->topk > 0 && !a->topk_idxs)) return SATTN_ERR_NULL_PTR;
+  if (a->kv_len > 0 && (!a->kv_fp8 || !a->kv_scale || (a->rope_dims > 0 && !a->kv_rope))) return SATTN_ERR_NULL_PTR;
+  if (a->sink_mode != SATTN_SINK_NONE && !a->sinks) return SATTN_ERR_NULL_PTR;
+  if (!aligned16(a->q) || !aligned16(a->o) || (a->kv_fp8 && !aligned16(a->kv_fp8)) ||
+      (a->kv_rope && !aligned16(a->kv_rope)) || (a->kv_scale && !aligned4(a->kv_scale)) ||
+      (a->topk_idxs && !aligned4(a->topk_idxs)) || (a->lse && !aligned4(a->lse)) || (a->sinks && !aligned4(a->sinks)))
+    return SATTN_ERR_ALIGNMENT;
+
+  sattn::IndexedParams p = {};
+  p.q = a->q;
+  p.kv = a->kv_fp8;
+  p.kv_scale = a->kv_scale;
+  p.kv_rope = a->kv_rope;
+  p.rope_dims = a->rope_dims;
+  p.idx = a->topk_idxs;
+  p.o = a->o;
+  p.lse = a->lse;
+  p.batch = a->batch;
+  p.q_len = a->q_len;
+  p.num_heads = a->num_heads;
+  p.head_dim = a->head_dim;
+  p.kv_len = a->kv_len;
+  p.topk = a->topk;
+  p.scale_log2 = a->softmax_scale * 1.4426950408889634f;
+  p.sinks = a->sink_mode != SATTN_SINK_NONE ? a->sinks : nullptr;
+  p.sink_mode = a->sink_mode;
+  p.num_parts = 1;
+  p.part_len = a->topk > 0 ? a->topk : 1;
+  if (!sattn::indexed_fp8_supported(p)) return SATTN_ERR_UNSUPPORTED;
+
+  if (a->num_splits == 1) return launch_status(sattn::launch_indexed_fp8(p, stream));
+  const size_t need = sattn_indexed_workspace_size(a->batch, a->q_len, a->num_heads, a->head_dim, a->num_splits);
+  if (!a->workspace || (reinterpret_cast<uintptr_t>(a->workspace) & 255u) || a->workspace_bytes < need)
+    return SATTN_ERR_WORKSPACE;
+  p.part_len = (a->topk + a->num_splits - 1) / a->num_splits;
+  const int parts = (a->topk + p.part_len - 1) / p.part_len;  // slices that hold at least one entry
+  if (parts == 1) {
+    p.part_len = a->topk;
+    return launch_status(sattn::launch_indexed_fp8(p, stream));
+  }
+  char *ws = static_cast<char *>(a->workspace);
+  p.num_parts = parts;
+  p.part_o = reinterpret_cast<float *>(ws);
+  p.part_lse = reinterpret_cast<float *>(ws + part_o_bytes(a->num_splits, rows, a->num_heads, a->head_dim));
+  if (sattn::launch_indexed_fp8(p, stream) != hipSuccess) return SATTN_ERR_LAUNCH;
+  sattn::MergeParams m;
+  m.part_o = p.part_o;
+  m.part_lse = p.part_lse;
+  m.num_parts = parts;
+  m.rows = static_cast<int>(rows);
+  m.num_heads = a->num_heads;
+  m.head_dim = a->head_dim;
+  m.sinks = p.sinks;
+  m.sink_mode = a->sink_mode == SATTN_SINK_NULL_LOGIT ? SATTN_SINK_NULL_LOGIT : SATTN_SINK_NONE;
+  m.out_type = sattn::kBF16;
+  m.o = a->o;
+  m.lse = a->lse;
+  return launch_status(sattn::launch_merge(m, stream));
+}
+
 }  // extern "C"

@@ -50,6 +50,10 @@ struct IndexedParams {
   const float *lse_in;  // [B*M, H] natural log, the normaliser
   float *mass;          // [B*M, H, n_bins]
   int block_keys, n_bins;
+  // fp8 cache launches (kv = e4m3 codes [B, N, D - rope_dims]):
+  const float *kv_scale;  // [B, N] one power-of-two scale per row
+  const void *kv_rope;    // [B, N, rope_dims] bf16, or null when rope_dims == 0
+  int rope_dims;
 };
 
 // Synthetic indexer: top-k compressed rows per query, after the window part of the list.
@@ -90,6 +94,8 @@ bool window_mfma_supported(const WindowParams &p);
 hipError_t launch_window_mfma(const WindowParams &p, hipStream_t stream);
 bool indexed_mfma_supported(const IndexedParams &p);
 hipError_t launch_indexed_mfma(const IndexedParams &p, hipStream_t stream);
+bool indexed_fp8_supported(const IndexedParams &p);
+hipError_t launch_indexed_fp8(const IndexedParams &p, hipStream_t stream);
 
 hipError_t launch_build_topk_idxs(const BuildIdxParams &p, hipStream_t stream);
 hipError_t launch_compress_pool(const CompressParams &p, int elem_type, hipStream_t stream);

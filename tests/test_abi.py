@@ -12,7 +12,7 @@ import pytest
 
 import sliding_window_attention_index_amd as sattn
 from sliding_window_attention_index_amd import (_BlockMassArgs, _BuildIdxArgs, _CompressArgs, _IndexedArgs,
-                                                 _IndexerArgs, _MergeArgs, _WindowArgs)
+                                                 _IndexedFp8Args, _IndexerArgs, _MergeArgs, _WindowArgs)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sattn.h")
@@ -37,7 +37,7 @@ def _declared_functions():
 def test_header_functions_exported(lib):
     names = _declared_functions()
     assert set(names) == {"sattn_window_fwd", "sattn_indexed_fwd", "sattn_merge_lse", "sattn_build_topk_idxs",
-                          "sattn_block_mass", "sattn_compress_pool", "sattn_indexer_topk",
+                          "sattn_block_mass", "sattn_compress_pool", "sattn_indexer_topk", "sattn_indexed_fp8_fwd",
                           "sattn_indexed_workspace_size", "sattn_status_string", "sattn_abi_version"}
     for name in names:
         assert hasattr(lib, name), name
@@ -278,3 +278,36 @@ def test_indexer_topk_empty_is_noop(lib):
     assert lib.sattn_indexer_topk(ctypes.byref(_ixr(batch=0, out=None)), None) == OK
     assert lib.sattn_indexer_topk(ctypes.byref(_ixr(q_len=0, qr=None)), None) == OK
     assert lib.sattn_indexer_topk(None, None) == NULL_PTR
+
+
+def _f8(**kw):
+    base = dict(q=FAKE, kv_fp8=FAKE, kv_scale=FAKE, kv_rope=FAKE, topk_idxs=FAKE, o=FAKE, lse=None, batch=1, q_len=8192,
+                num_heads=32, head_dim=128, rope_dims=64, kv_len=8320, topk=640, softmax_scale=0.088, sinks=None,
+                sink_mode=0, num_splits=1, workspace=None, workspace_bytes=0)
+    base.update(kw)
+    return _IndexedFp8Args(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=64), UNSUPPORTED),
+    (dict(rope_dims=32), UNSUPPORTED),
+    (dict(num_heads=48), UNSUPPORTED),
+    (dict(softmax_scale=-1.0), UNSUPPORTED),
+    (dict(rope_dims=129), SHAPE),
+    (dict(batch=-1), SHAPE),
+    (dict(sink_mode=7), ARG),
+    (dict(num_splits=0), ARG),
+    (dict(kv_scale=None), NULL_PTR),
+    (dict(kv_rope=None), NULL_PTR),
+    (dict(sink_mode=2), NULL_PTR),
+    (dict(kv_fp8=FAKE + 8), ALIGNMENT),
+    (dict(kv_scale=FAKE + 2), ALIGNMENT),
+    (dict(num_splits=8), WORKSPACE),
+])
+def test_indexed_fp8_validation(lib, kw, status):
+    assert lib.sattn_indexed_fp8_fwd(ctypes.byref(_f8(**kw)), None) == status
+
+
+def test_indexed_fp8_empty_is_noop(lib):
+    assert lib.sattn_indexed_fp8_fwd(ctypes.byref(_f8(batch=0, q=None)), None) == OK
+    assert lib.sattn_indexed_fp8_fwd(None, None) == NULL_PTR
