@@ -20,9 +20,10 @@
 //     tiles of a sequence, which read mostly the same keys, meet in that XCD's
 //     L2.
 //   * K and V blocks arrive by direct global->LDS DMA (buffer_load ... lds)
-//     into a ring of 4 swizzled slots (K tile + V tile) shared by the four
-//     waves; each wave fetches a quarter of every slot.  Block j + 3 is
-//     requested while block j is computed.  Requests past the last block
+//     into a ring of swizzled slots (K tile + V tile; 3 slots at D = 128, so
+//     that three workgroups share a CU, 4 at D = 64) shared by the four
+//     waves; each wave fetches a quarter of every slot.  Block j + slots - 1
+//     is requested while block j is computed.  Requests past the last block
 //     point outside the buffer (they move no data), so every step waits for
 //     the same number of this wave's requests; one barrier per step then
 //     publishes the slot and frees the one read in the step before.
@@ -44,7 +45,6 @@ namespace {
 
 constexpr int kBlockKeys = 32;
 constexpr int kXcds = 8;
-constexpr int kRing = 4;
 constexpr uint32_t kNoData = 0x80000000u;  // a buffer offset past every valid range
 
 template <int I>
@@ -53,8 +53,14 @@ struct Idx {
 };
 
 template <int D, int G>
-__global__ __launch_bounds__(256) void window_fwd_mfma(WindowParams p, int tiles_per_seq, int n_tiles) {
+__global__ __launch_bounds__(256, D == 128 && (G <= 4 || G == 32) ? 3 : 1) void window_fwd_mfma(WindowParams p, int tiles_per_seq, int n_tiles) {
   using Tile = SwizzledTile<D>;
+  // D = 128 runs three workgroups per CU: a 3-slot ring (48 KB of LDS) and LDS addresses derived
+  // by XOR from one base per operand instead of one register per read (168 VGPRs; G = 8 and 16
+  // index their rows with a few more registers and stay at two).  D = 64 keeps four slots and
+  // precomputed addresses (four workgroups per CU either way).
+  constexpr int kRing = D == 128 ? 3 : 4;
+  constexpr bool kXorAddr = D == 128;
   constexpr int S = D / 16;
   constexpr int DB = D / 32;
   constexpr int QW = 32 / G;                  // queries per wave
@@ -142,10 +148,20 @@ __global__ __launch_bounds__(256) void window_fwd_mfma(WindowParams p, int tiles
   }
   issue(Idx<0>{}, 0);
   issue(Idx<1>{}, 1);
-  issue(Idx<2>{}, 2);
+  if constexpr (kRing == 4) issue(Idx<2>{}, 2);
 
-  // ---- per-lane LDS read offsets: K rows (A operand) and V^T quads ----
+  // ---- per-lane LDS read offsets: K rows (A operand) and V^T quads.  With XOR addressing (bits 4..7
+  // of every tile base are clear): row n's logical chunk h S + s at kbase ^ 16 s; V^T quads at
+  // vbase ^ (64 db + 16 e) plus rows 8 e + 16 tt ----
   const uint32_t ring_addr = lds_addr(ring);
+  const uint32_t kbase = ring_addr + Tile::offset(n, h * S);
+  uint32_t vbase;
+  {
+    const int g16 = lane >> 4, i16 = lane & 15;
+    const int c2 = 2 * (g16 & 1) + ((i16 & 3) >> 1);
+    vbase = ring_addr + Tile::kBytes + Tile::offset(4 * h + (i16 >> 2), c2) + (i16 & 1) * 8;
+  }
+  constexpr int kRow8 = 8 * Tile::kRowBytes;
   uint32_t koff[S];
 #pragma unroll
   for (int s = 0; s < S; ++s) koff[s] = ring_addr + Tile::offset(n, h * S + s);
@@ -173,8 +189,15 @@ __global__ __launch_bounds__(256) void window_fwd_mfma(WindowParams p, int tiles
   auto compute_block = [&](auto I, int kb0) {
     constexpr int off = decltype(I)::value * kSlot;
     u32x4 kf[S];
+    if constexpr (kXorAddr) {
+      uint32_t kb_ = kbase;  // opaque per block: the XORed addresses stay local
+      asm volatile("" : "+v"(kb_));
 #pragma unroll
-    for (int s = 0; s < S; ++s) kf[s] = ds_read_b128<off>(koff[s]);
+      for (int s = 0; s < S; ++s) kf[s] = ds_read_b128<off>(kb_ ^ (16u * s));
+    } else {
+#pragma unroll
+      for (int s = 0; s < S; ++s) kf[s] = ds_read_b128<off>(koff[s]);
+    }
     lgkm_fence<0>(kf);
     f32x16 st = f32x16{};
 #pragma unroll
@@ -182,12 +205,24 @@ __global__ __launch_bounds__(256) void window_fwd_mfma(WindowParams p, int tiles
       st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[s]), qf[s], st, 0, 0, 0);
     // V^T quads: read while the QK products and the softmax run (the K rows are dead by then).
     u32x2 vr[4 * DB];
+    if constexpr (kXorAddr) {
+      uint32_t vb = vbase;
+      asm volatile("" : "+v"(vb));
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+      for (int db = 0; db < DB; ++db) {
+        vr[db * 2] = ds_read_tr_b16<off>(vb ^ (64u * db));
+        vr[db * 2 + 1] = ds_read_tr_b16<off + kRow8>(vb ^ (64u * db + 16u));
+        vr[2 * DB + db * 2] = ds_read_tr_b16<off + 2 * kRow8>(vb ^ (64u * db));
+        vr[2 * DB + db * 2 + 1] = ds_read_tr_b16<off + 3 * kRow8>(vb ^ (64u * db + 16u));
+      }
+    } else {
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int e = 0; e < 2; ++e) vr[(tt * DB + db) * 2 + e] = ds_read_tr_b16<off>(voff[tt][db][e]);
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int e = 0; e < 2; ++e) vr[(tt * DB + db) * 2 + e] = ds_read_tr_b16<off>(voff[tt][db][e]);
+    }
     // Element r of lane (n, h) is key kb0 + 8*(r/4) + 4h + r%4 for this lane's row.
     if (p.sink_mode == kSinkKey0 && kb0 == 0 && h == 0) st[0] += sink_raw;
     const int kb1 = kb0 + kBlockKeys - 1;
@@ -215,12 +250,12 @@ __global__ __launch_bounds__(256) void window_fwd_mfma(WindowParams p, int tiles
       }
   };
 
-  // Step j: block j is in slot j % 4.  This wave's requests younger than block j's are those of
-  // blocks j + 1 and j + 2 (block j + 3 is requested after the barrier), so one fixed wait covers
-  // every step, the first included (it then also waits for block 1).
+  // Step j: block j is in slot j % kRing.  This wave's requests younger than block j's are those of
+  // blocks j + 1 .. j + kRing - 2 (block j + kRing - 1 is requested after the barrier), so one
+  // fixed wait covers every step, the first included.
   auto step = [&](auto I, int j) {
     constexpr int i = decltype(I)::value;
-    wait_vmcnt<2 * kDmaPerSlot>();
+    wait_vmcnt<(kRing - 2) * kDmaPerSlot>();
     __builtin_amdgcn_s_barrier();
     issue(Idx<(i + kRing - 1) % kRing>{}, j + kRing - 1);  // the slot block j - 1 was read from
     const int kb0 = lo_wg + j * kBlockKeys;
@@ -232,8 +267,10 @@ __global__ __launch_bounds__(256) void window_fwd_mfma(WindowParams p, int tiles
     step(Idx<1>{}, j + 1);
     if (j + 2 >= nblk) break;
     step(Idx<2>{}, j + 2);
-    if (j + 3 >= nblk) break;
-    step(Idx<3>{}, j + 3);
+    if constexpr (kRing == 4) {
+      if (j + 3 >= nblk) break;
+      step(Idx<3>{}, j + 3);
+    }
   }
 
   // ---- epilogue: o = acc / l and lse, through the ring once every wave is done with it ----
