@@ -40,6 +40,7 @@ namespace {
 
 constexpr int kBlockKeys = 32;
 constexpr int kIdxCap = 1024;  // list entries staged per wave at a time
+constexpr uint32_t kBadRow = 0xfffff000u;  // staged offset of an entry that is not a row: past every buffer
 
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -142,10 +143,7 @@ __global__ __launch_bounds__(256) void indexed_fwd_mfma(IndexedParams p) {
     for (int u = 0; u < kU; ++u) {
       int row, chunk;
       Tile::dma_source(u, lane, row, chunk);  // row == u * kR + dg
-      const int x = static_cast<int>(e4[u / 4][u % 4]);
-      const bool valid = x >= 0 && x < N;
-      const uint32_t off = valid ? static_cast<uint32_t>(x) * Tile::kRowBytes + chunk * 16 : 0xfffff000u;
-      dma16(krs, dst + u * 1024, off);
+      dma16(krs, dst + u * 1024, e4[u / 4][u % 4] | static_cast<uint32_t>(chunk * 16));  // kBadRow stays out of range
     }
   };
 
@@ -224,8 +222,9 @@ __global__ __launch_bounds__(256) void indexed_fwd_mfma(IndexedParams p) {
     const int cend = min(ke, c0 + kIdxCap);
     const int nblk = (cend - c0 + kBlockKeys - 1) / kBlockKeys;
     asm volatile("" ::: "memory");  // the previous chunk's list reads (inline asm) stay before these stores
-    // Stage the chunk's entries (-1 past its end).  Every DMA of the previous chunk has been
-    // waited for, so nothing reads or fills LDS meanwhile.
+    // Stage the chunk's entries as byte offsets of their rows (kBadRow for -1, out-of-range
+    // entries and past the chunk's end).  Every DMA of the previous chunk has been waited for, so
+    // nothing reads or fills LDS meanwhile.
     {
       // 16 bytes per lane per load, every load issued before any is used.
       constexpr int kLoads = kIdxCap / 256;
@@ -242,7 +241,10 @@ __global__ __launch_bounds__(256) void indexed_fwd_mfma(IndexedParams p) {
         if (j < nblk * kBlockKeys) {
           u32x4 w;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = c0 + j + e < cend ? v[i][e] : 0xffffffffu;
+          for (int e = 0; e < 4; ++e) {
+            const int x = static_cast<int>(v[i][e]);
+            w[e] = c0 + j + e < cend && x >= 0 && x < N ? static_cast<uint32_t>(x) * Tile::kRowBytes : kBadRow;
+          }
           *reinterpret_cast<u32x4 *>(list + j) = w;
         }
       }
@@ -259,10 +261,9 @@ __global__ __launch_bounds__(256) void indexed_fwd_mfma(IndexedParams p) {
       else if (younger == 2) wait_vmcnt<2 * kDpb>();
       else if (younger == 1) wait_vmcnt<kDpb>();
       else wait_vmcnt<0>();
-      const int x = ds_read_i32(list_addr + (j * kBlockKeys + entry_of_row(n)) * 4);  // tile row n's entry
-      const bool valid = x >= 0 && x < N;
-      const uint32_t vmask = static_cast<uint32_t>(__ballot(valid));
-      const uint32_t zmask = key0 ? static_cast<uint32_t>(__ballot(valid && x == 0)) : 0u;
+      const uint32_t x = static_cast<uint32_t>(ds_read_i32(list_addr + (j * kBlockKeys + entry_of_row(n)) * 4));
+      const uint32_t vmask = static_cast<uint32_t>(__ballot(x != kBadRow));  // tile row n's entry is a row
+      const uint32_t zmask = key0 ? static_cast<uint32_t>(__ballot(x == 0u)) : 0u;  // ... and it is row 0
       if (vmask != 0u) compute(j & (NT - 1), vmask, zmask);
       if constexpr (kMass) {
         if (--bin_left == 0 || (j == nblk - 1 && cend == ke)) {  // the block ends with this tile
