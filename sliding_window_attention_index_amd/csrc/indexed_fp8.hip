@@ -26,6 +26,10 @@ namespace {
 
 constexpr int kBlockKeys = 32;
 constexpr int kIdxCap = 512;  // list entries staged per wave at a time
+// Staged stand-in for an entry that is not a row: times any of the row sizes used here (4, 64, 128
+// bytes, modulo 2^32), plus an in-row offset below 128, it lands at 0xfffe0000 or above, past the
+// end of every buffer (all are < 2^31) and far from wrapping.
+constexpr uint32_t kBadRow = 0x3ffffc00u;
 
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -157,22 +161,19 @@ __global__ __launch_bounds__(256) void indexed_fp8_mfma(IndexedParams p) {
     }
     xs[kReads - 1] = ds_read_b32_raw(lbase + (lane & (kBlockKeys - 1)) * 4);
     lgkm_fence<0>(xs);
-    auto valid = [&](uint32_t x) { return static_cast<int>(x) >= 0 && static_cast<int>(x) < N; };
 #pragma unroll
-    for (int u = 0; u < kF8Dma; ++u) {
-      const uint32_t off = valid(xs[u]) ? xs[u] * D8 + (lane % kF8LanesPerRow) * 16 : 0xfffff000u;
-      dma16(f8rs, slot + kRopeBytes + u * 1024, off);
-    }
+    for (int u = 0; u < kF8Dma; ++u)
+      dma16(f8rs, slot + kRopeBytes + u * 1024, xs[u] * D8 + (lane % kF8LanesPerRow) * 16);
 #pragma unroll
     for (int u = 0; u < kRopeDma; ++u) {
       int row, chunk;
       T64::dma_source(u, lane, row, chunk);
       const uint32_t x = xs[kF8Dma + u];
-      dma16(rprs, slot + u * 1024, valid(x) ? x * (RD * 2) + chunk * 16 : 0xfffff000u);
+      dma16(rprs, slot + u * 1024, x * (RD * 2) + chunk * 16);
     }
     {
       const uint32_t x = xs[kReads - 1];
-      dma4(scrs, slot + kRopeBytes + kF8Bytes, lane < kBlockKeys && valid(x) ? x * 4u : 0xfffff000u);
+      dma4(scrs, slot + kRopeBytes + kF8Bytes, lane < kBlockKeys ? x * 4u : 0xfffff000u);
     }
   };
 
@@ -267,8 +268,8 @@ __global__ __launch_bounds__(256) void indexed_fp8_mfma(IndexedParams p) {
     const int cend = min(ke, c0 + kIdxCap);
     const int nblk = (cend - c0 + kBlockKeys - 1) / kBlockKeys;
     asm volatile("" ::: "memory");  // the previous chunk's list reads (inline asm) stay before these stores
-    // Stage the chunk's entries (-1 past its end).  Every DMA of the previous chunk has been
-    // waited for, so nothing reads or fills LDS meanwhile.
+    // Stage the chunk's entries (kBadRow for -1, out-of-range entries and past the chunk's end).
+    // Every DMA of the previous chunk has been waited for, so nothing reads or fills LDS meanwhile.
     {
       constexpr int kLoads = kIdxCap / 256;
       u32x4 v[kLoads];
@@ -284,7 +285,10 @@ __global__ __launch_bounds__(256) void indexed_fp8_mfma(IndexedParams p) {
         if (j < nblk * kBlockKeys) {
           u32x4 w;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = c0 + j + e < cend ? v[i][e] : 0xffffffffu;
+          for (int e = 0; e < 4; ++e) {
+            const int x = static_cast<int>(v[i][e]);
+            w[e] = c0 + j + e < cend && x >= 0 && x < N ? static_cast<uint32_t>(x) : kBadRow;
+          }
           *reinterpret_cast<u32x4 *>(list + j) = w;
         }
       }
@@ -301,10 +305,9 @@ __global__ __launch_bounds__(256) void indexed_fp8_mfma(IndexedParams p) {
       else if (younger == 2) wait_vmcnt<2 * kDpb>();
       else if (younger == 1) wait_vmcnt<kDpb>();
       else wait_vmcnt<0>();
-      const int x = ds_read_i32(list_addr + (j * kBlockKeys + n) * 4);  // tile row n's entry
-      const bool valid = x >= 0 && x < N;
-      const uint32_t vmask = static_cast<uint32_t>(__ballot(valid));
-      const uint32_t zmask = key0 ? static_cast<uint32_t>(__ballot(valid && x == 0)) : 0u;
+      const uint32_t x = static_cast<uint32_t>(ds_read_i32(list_addr + (j * kBlockKeys + n) * 4));
+      const uint32_t vmask = static_cast<uint32_t>(__ballot(x != kBadRow));  // tile row n's entry is a row
+      const uint32_t zmask = key0 ? static_cast<uint32_t>(__ballot(x == 0u)) : 0u;  // ... and it is row 0
       if (vmask != 0u) {
         convert_block(j & (NT - 1));
         compute(j & (NT - 1), vmask, zmask);
