@@ -6,9 +6,12 @@
 // position p lives in ring slot p % window, and compressed row c exists once
 // position (c + 1) * ratio - 1 has been seen.  Unused entries are -1.
 //
-// The lists are pure integer functions of (position, entry), so the kernel is
-// a store stream: one thread writes four consecutive entries of one list
-// (one 16-byte store when rows allow it), HBM-write bound.
+// The lists are pure integer functions of (position, entry), so the kernels are
+// store streams.  Lists of at least 256 entries with 16-byte aligned rows: one
+// wave per list at a time works out the list's window start, ring slot and
+// number of visible compressed rows once, then each lane writes 16-byte pieces
+// with a compare and a select per entry.  Other shapes: one thread per four
+// consecutive entries of one list.
 #include <algorithm>
 
 #include "sattn_device.hpp"
@@ -51,6 +54,43 @@ __global__ __launch_bounds__(256) void build_topk_idxs_kernel(BuildIdxParams a) 
   }
 }
 
+// One wave per list (K % 4 == 0, 16-byte aligned rows).
+__global__ __launch_bounds__(256) void build_topk_idxs_rows(BuildIdxParams a) {
+  const int W = a.window;
+  const int K = W + a.n_comp;
+  const int per_row = K / 4;
+  const int64_t rows = static_cast<int64_t>(a.batch) * a.q_len;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int lane = static_cast<int>(threadIdx.x & 63);
+  for (int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + wave; r < rows; r += static_cast<int64_t>(gridDim.x) * 4) {
+    const int64_t b = r / a.q_len;
+    const int64_t p = static_cast<int64_t>(a.start_pos[b]) + (r - b * a.q_len);
+    // Window part: entry k is position q0 + k, listed (as ring slot (q0 + k) % W) while q0 + k <= p,
+    // that is for k < nw.  Compressed part: row c is visible once (c + 1) ratio - 1 <= p, that is
+    // for c < (p + 1) / ratio.
+    const int64_t q0 = p - W + 1 > 0 ? p - W + 1 : 0;
+    const int nw = p < 0 ? 0 : static_cast<int>(p + 1 < W ? p + 1 : W);
+    const int s0 = W > 0 ? static_cast<int>(q0 % W) : 0;
+    const int64_t vis = a.ratio > 0 && p >= 0 ? (p + 1) / a.ratio : 0;
+    const int nc = static_cast<int>(vis < a.n_comp ? vis : a.n_comp);
+    int32_t *dst = a.out + r * K;
+    for (int ch = lane; ch < per_row; ch += 64) {
+      i32x4 v;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int k = 4 * ch + j;
+        if (k < W) {
+          const int slot = s0 + k >= W ? s0 + k - W : s0 + k;
+          v[j] = k < nw ? slot : -1;
+        } else {
+          v[j] = k - W < nc ? k : -1;  // row W + c of the cache is entry W + c
+        }
+      }
+      *reinterpret_cast<i32x4 *>(dst + 4 * ch) = v;
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_build_topk_idxs(const BuildIdxParams &a, hipStream_t stream) {
@@ -61,8 +101,14 @@ hipError_t launch_build_topk_idxs(const BuildIdxParams &a, hipStream_t stream) {
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
-  const int64_t blocks = std::min<int64_t>((total + 255) / 256, static_cast<int64_t>(cus) * 16);
   const bool vec = K % 4 == 0 && (reinterpret_cast<uintptr_t>(a.out) & 15u) == 0;
+  if (vec && K >= 256) {
+    const int64_t rows = static_cast<int64_t>(a.batch) * a.q_len;
+    const int64_t wgs = std::min<int64_t>((rows + 3) / 4, static_cast<int64_t>(cus) * 16);
+    hipLaunchKernelGGL(build_topk_idxs_rows, dim3(static_cast<unsigned>(wgs)), dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
+  const int64_t blocks = std::min<int64_t>((total + 255) / 256, static_cast<int64_t>(cus) * 16);
   if (vec)
     hipLaunchKernelGGL(build_topk_idxs_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, a);
   else
