@@ -8,9 +8,10 @@
 //
 // The lists are pure integer functions of (position, entry), so the kernels are
 // store streams.  Lists of at least 256 entries with 16-byte aligned rows: one
-// wave per list at a time works out the list's window start, ring slot and
-// number of visible compressed rows once, then each lane writes 16-byte pieces
-// with a compare and a select per entry.  Other shapes: one thread per four
+// wave per piece of a list (up to 4 KB) works out the list's window start, ring
+// slot and number of visible compressed rows once, then each lane writes 16-byte
+// chunks with a compare and a select per entry; many small pieces keep enough
+// stores in flight.  Other shapes: one thread per four
 // consecutive entries of one list.
 #include <algorithm>
 
@@ -54,15 +55,20 @@ __global__ __launch_bounds__(256) void build_topk_idxs_kernel(BuildIdxParams a) 
   }
 }
 
-// One wave per list (K % 4 == 0, 16-byte aligned rows).
+// One wave per piece of kPiece 16-byte chunks of a list (K % 4 == 0, 16-byte aligned rows).
+constexpr int kPiece = 256;
 __global__ __launch_bounds__(256) void build_topk_idxs_rows(BuildIdxParams a) {
   const int W = a.window;
   const int K = W + a.n_comp;
   const int per_row = K / 4;
-  const int64_t rows = static_cast<int64_t>(a.batch) * a.q_len;
+  const int pieces = (per_row + kPiece - 1) / kPiece;
+  const int64_t items = static_cast<int64_t>(a.batch) * a.q_len * pieces;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int lane = static_cast<int>(threadIdx.x & 63);
-  for (int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + wave; r < rows; r += static_cast<int64_t>(gridDim.x) * 4) {
+  for (int64_t w = static_cast<int64_t>(blockIdx.x) * 4 + wave; w < items; w += static_cast<int64_t>(gridDim.x) * 4) {
+    const int64_t r = w / pieces;
+    const int ch0 = static_cast<int>(w - r * pieces) * kPiece;
+    const int ch1 = per_row < ch0 + kPiece ? per_row : ch0 + kPiece;
     const int64_t b = r / a.q_len;
     const int64_t p = static_cast<int64_t>(a.start_pos[b]) + (r - b * a.q_len);
     // Window part: entry k is position q0 + k, listed (as ring slot (q0 + k) % W) while q0 + k <= p,
@@ -74,7 +80,7 @@ __global__ __launch_bounds__(256) void build_topk_idxs_rows(BuildIdxParams a) {
     const int64_t vis = a.ratio > 0 && p >= 0 ? (p + 1) / a.ratio : 0;
     const int nc = static_cast<int>(vis < a.n_comp ? vis : a.n_comp);
     int32_t *dst = a.out + r * K;
-    for (int ch = lane; ch < per_row; ch += 64) {
+    for (int ch = ch0 + lane; ch < ch1; ch += 64) {
       i32x4 v;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -103,8 +109,8 @@ hipError_t launch_build_topk_idxs(const BuildIdxParams &a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const bool vec = K % 4 == 0 && (reinterpret_cast<uintptr_t>(a.out) & 15u) == 0;
   if (vec && K >= 256) {
-    const int64_t rows = static_cast<int64_t>(a.batch) * a.q_len;
-    const int64_t wgs = std::min<int64_t>((rows + 3) / 4, static_cast<int64_t>(cus) * 16);
+    const int64_t items = static_cast<int64_t>(a.batch) * a.q_len * ((K / 4 + kPiece - 1) / kPiece);
+    const int64_t wgs = std::min<int64_t>((items + 3) / 4, static_cast<int64_t>(cus) * 1024);  // ~one piece per wave
     hipLaunchKernelGGL(build_topk_idxs_rows, dim3(static_cast<unsigned>(wgs)), dim3(256), 0, stream, a);
     return hipGetLastError();
   }
