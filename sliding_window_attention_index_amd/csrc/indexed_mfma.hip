@@ -215,9 +215,24 @@ __global__ __launch_bounds__(256) void indexed_fwd_mfma(IndexedParams p) {
 
   // Block mass: blocks of block_keys entries are whole runs of 32-entry tiles (block_keys % 32 == 0
   // and every slice starts on a block boundary); `bin_left` tiles of the current block remain.
+  // Finished blocks' masses wait in registers (up to kMassBuf) and are written together, so that a
+  // task's masses reach memory in whole lines rather than one 4-byte store per block.
+  constexpr int kMassBuf = 16;
   const int tiles_per_bin = kMass ? p.block_keys / kBlockKeys : 1;
-  int bin = kMass ? kb / p.block_keys : 0;
+  int bin = kMass ? kb / p.block_keys : 0;  // first block not yet written
   int bin_left = tiles_per_bin;
+  float mbuf[kMass ? kMassBuf : 1];
+  int nbuf = 0;
+  auto flush_masses = [&]() {
+    if (h == 0) {
+      float *dst = p.mass + (bt * H + head0 + n) * p.n_bins + bin;
+#pragma unroll
+      for (int k = 0; k < kMassBuf; ++k)
+        if (k < nbuf) dst[k] = mbuf[k];
+    }
+    bin += nbuf;
+    nbuf = 0;
+  };
   for (int c0 = kb; c0 < ke; c0 += kIdxCap) {
     const int cend = min(ke, c0 + kIdxCap);
     const int nblk = (cend - c0 + kBlockKeys - 1) / kBlockKeys;
@@ -268,9 +283,10 @@ __global__ __launch_bounds__(256) void indexed_fwd_mfma(IndexedParams p) {
       if constexpr (kMass) {
         if (--bin_left == 0 || (j == nblk - 1 && cend == ke)) {  // the block ends with this tile
           const float tot = halves_sum(bin_sum);
-          if (h == 0) p.mass[(bt * H + head0 + n) * p.n_bins + bin] = tot;
+#pragma unroll
+          for (int k = 0; k < kMassBuf; ++k) mbuf[k] = k == nbuf ? tot : mbuf[k];
+          if (++nbuf == kMassBuf) flush_masses();
           bin_sum = 0.0f;
-          ++bin;
           bin_left = tiles_per_bin;
         }
       }
@@ -278,6 +294,7 @@ __global__ __launch_bounds__(256) void indexed_fwd_mfma(IndexedParams p) {
     }
   }
 
+  if constexpr (kMass) flush_masses();
   if constexpr (!kMass) {
     // Epilogue: o = acc / l, lse = ln(2) * (m + log2 l).  Lane (n, h) holds dims 32db + 8j + 4h + {0..3}
     // of head n.  Each 32-dim block goes through the wave's first tile as scaled fp32 (16-byte chunk

@@ -39,6 +39,9 @@ SMALL = [
     ([-5, -1, 0], 8, 4, 1, 3),           # negative positions see nothing until 0
     ([127, 128, 129], 3, 128, 4, 64),    # around the ring wrap
     ([24576], 64, 128, 4, 8192),         # the prefill configuration's first queries
+    ([-3, 0, 300, 5000], 5, 4, 2, 1024), # K = 1028: one wave per 4 KB piece, the last piece one chunk
+    ([-3, 10, 600], 4, 4, 2, 252),       # K = 256: one piece, mostly compressed rows
+    ([1000, 255], 3, 256, 0, 0),         # K = 256, window only, the ring slot wrapping inside a piece
 ]
 
 
