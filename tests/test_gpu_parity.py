@@ -56,6 +56,8 @@ WINDOW_CASES = [
     ("gqa16", [80, 40], 16, 1, 128, (20, 20), W.SINK_NONE, torch.bfloat16),
     ("gqa32", [50], 32, 1, 64, (10, 0), W.SINK_NULL, torch.bfloat16),
     ("gqa4_d64", [200, 33], 16, 4, 64, (64, 64), W.SINK_KEY0, torch.bfloat16),
+    ("mha_d128", [130, 65], 4, 4, 128, (40, 40), W.SINK_NULL, torch.bfloat16),
+    ("gqa8_d128", [300, 7], 16, 2, 128, (127, 0), W.SINK_KEY0, torch.bfloat16),
     ("empty_seqs", [0, 40, 0, 1, 0], 4, 2, 64, (8, 8), W.SINK_KEY0, torch.bfloat16),
     ("valu_gqa3", [60, 9], 6, 2, 64, (7, 7), W.SINK_KEY0, torch.bfloat16),
     ("valu_d96", [45], 4, 2, 96, (5, 5), W.SINK_NULL, torch.bfloat16),
