@@ -150,33 +150,32 @@ __global__ __launch_bounds__(256, D == 128 && (G <= 4 || G == 32) ? 3 : 1) void 
   issue(Idx<1>{}, 1);
   if constexpr (kRing == 4) issue(Idx<2>{}, 2);
 
-  // ---- per-lane LDS read offsets: K rows (A operand) and V^T quads.  With XOR addressing (bits 4..7
-  // of every tile base are clear): row n's logical chunk h S + s at kbase ^ 16 s; V^T quads at
-  // vbase ^ (64 db + 16 e) plus rows 8 e + 16 tt ----
+  // ---- per-lane LDS read addresses of the K rows (A operand) and V^T quads.  XOR addressing (D = 128;
+  // bits 4..7 of every tile base are clear): row n's logical chunk h S + s at kbase ^ 16 s, V^T quads
+  // at vbase ^ (64 db + 16 e) plus rows 8 e + 16 tt.  Otherwise one precomputed register per read
+  // (koff, voff). ----
   const uint32_t ring_addr = lds_addr(ring);
-  const uint32_t kbase = ring_addr + Tile::offset(n, h * S);
-  uint32_t vbase;
-  {
-    const int g16 = lane >> 4, i16 = lane & 15;
-    const int c2 = 2 * (g16 & 1) + ((i16 & 3) >> 1);
-    vbase = ring_addr + Tile::kBytes + Tile::offset(4 * h + (i16 >> 2), c2) + (i16 & 1) * 8;
-  }
-  constexpr int kRow8 = 8 * Tile::kRowBytes;
-  uint32_t koff[S];
-#pragma unroll
-  for (int s = 0; s < S; ++s) koff[s] = ring_addr + Tile::offset(n, h * S + s);
   const int g16 = lane >> 4, i16 = lane & 15;
+  const uint32_t kbase = ring_addr + Tile::offset(n, h * S);
+  const uint32_t vbase = ring_addr + Tile::kBytes +
+                         Tile::offset(4 * h + (i16 >> 2), 2 * (g16 & 1) + ((i16 & 3) >> 1)) + (i16 & 1) * 8;
+  constexpr int kRow8 = 8 * Tile::kRowBytes;
+  uint32_t koff[kXorAddr ? 1 : S];
   uint32_t voff[2][DB][2];
+  if constexpr (!kXorAddr) {
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
+    for (int s = 0; s < S; ++s) koff[s] = ring_addr + Tile::offset(n, h * S + s);
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int row = 16 * tt + 4 * h + (i16 >> 2) + 8 * e;
-        const int chunk = 4 * db + 2 * (g16 & 1) + ((i16 & 3) >> 1);
-        voff[tt][db][e] = ring_addr + Tile::kBytes + Tile::offset(row, chunk) + (i16 & 1) * 8;
-      }
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int row = 16 * tt + 4 * h + (i16 >> 2) + 8 * e;
+          const int chunk = 4 * db + 2 * (g16 & 1) + ((i16 & 3) >> 1);
+          voff[tt][db][e] = ring_addr + Tile::kBytes + Tile::offset(row, chunk) + (i16 & 1) * 8;
+        }
+  }
 
   const float sink_raw = sink * kLog2e / c;  // the running max is kept in raw logit units
   f32x16 acc[DB];
