@@ -33,6 +33,13 @@ EXTRA_FLAGS = {
     "window_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
+# Kernels that count their own outstanding LDS-DMA requests (fixed s_waitcnt vmcnt values) must
+# not spill: a compiler-inserted scratch access is one more vector-memory operation in flight and
+# would make those waits return early.  The build reads the compiler's resource report for these
+# sources and fails on any scratch use.
+NO_SCRATCH = {"indexed_mfma.hip", "indexed_fp8.hip", "window_mfma.hip", "indexer.hip"}
+_USAGE = "kernel-resource-usage"
+
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}",
     "-O3",
@@ -52,13 +59,26 @@ def _compile(src: str, verbose: bool) -> str:
     if src.endswith(".cpp"):
         cmd += ["-x", "hip"]
     cmd += EXTRA_FLAGS.get(src, [])
+    if src in NO_SCRATCH:
+        cmd += [f"-Rpass-analysis={_USAGE}"]
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    err = "\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l)
+    lines = [l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l]
+    err = "\n".join(l for l in lines if _USAGE not in l)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{err}")
+    if src in NO_SCRATCH:
+        fn, bad = "?", []
+        for l in lines:
+            if "Function Name:" in l:
+                fn = l.split("Function Name:")[1].split("[")[0].strip()
+            elif "ScratchSize [bytes/lane]:" in l or "VGPRs Spill:" in l:  # (SGPRs spill into VGPR lanes)
+                if int(l.split(":")[-1].split("[")[0]) != 0:
+                    bad.append(f"{fn}: {l.split('remark:')[1].split('[-R')[0].strip()}")
+        if bad:
+            raise RuntimeError(f"{src}: kernels that count their own memory requests use scratch:\n" + "\n".join(bad))
     if verbose and err.strip():
         print(err, file=sys.stderr)
     return obj
