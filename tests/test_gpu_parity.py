@@ -58,6 +58,8 @@ WINDOW_CASES = [
     ("gqa4_d64", [200, 33], 16, 4, 64, (64, 64), W.SINK_KEY0, torch.bfloat16),
     ("mha_d128", [130, 65], 4, 4, 128, (40, 40), W.SINK_NULL, torch.bfloat16),
     ("gqa8_d128", [300, 7], 16, 2, 128, (127, 0), W.SINK_KEY0, torch.bfloat16),
+    ("gqa16_d64", [90, 31], 16, 1, 64, (15, 15), W.SINK_NULL, torch.bfloat16),
+    ("gqa2_d64", [260, 3], 8, 4, 64, (32, 64), W.SINK_KEY0, torch.bfloat16),
     ("empty_seqs", [0, 40, 0, 1, 0], 4, 2, 64, (8, 8), W.SINK_KEY0, torch.bfloat16),
     ("valu_gqa3", [60, 9], 6, 2, 64, (7, 7), W.SINK_KEY0, torch.bfloat16),
     ("valu_d96", [45], 4, 2, 96, (5, 5), W.SINK_NULL, torch.bfloat16),
