@@ -53,6 +53,19 @@ COMMON_FLAGS = [
 ]
 
 
+def scratch_users(report_lines) -> list[str]:
+    """Kernels of a `-Rpass-analysis=kernel-resource-usage` report that use scratch memory or spill
+    VGPRs (SGPR spills go to VGPR lanes and are not counted)."""
+    fn, bad = "?", []
+    for l in report_lines:
+        if "Function Name:" in l:
+            fn = l.split("Function Name:")[1].split("[")[0].strip()
+        elif "ScratchSize [bytes/lane]:" in l or "VGPRs Spill:" in l:
+            if int(l.split(":")[-1].split("[")[0]) != 0:
+                bad.append(f"{fn}: {l.split('remark:')[1].split('[-R')[0].strip()}")
+    return bad
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
     cmd = [HIPCC, *COMMON_FLAGS]
@@ -70,13 +83,7 @@ def _compile(src: str, verbose: bool) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{err}")
     if src in NO_SCRATCH:
-        fn, bad = "?", []
-        for l in lines:
-            if "Function Name:" in l:
-                fn = l.split("Function Name:")[1].split("[")[0].strip()
-            elif "ScratchSize [bytes/lane]:" in l or "VGPRs Spill:" in l:  # (SGPRs spill into VGPR lanes)
-                if int(l.split(":")[-1].split("[")[0]) != 0:
-                    bad.append(f"{fn}: {l.split('remark:')[1].split('[-R')[0].strip()}")
+        bad = scratch_users(lines)
         if bad:
             raise RuntimeError(f"{src}: kernels that count their own memory requests use scratch:\n" + "\n".join(bad))
     if verbose and err.strip():
