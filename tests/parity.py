@@ -30,7 +30,8 @@ def compare(got: torch.Tensor, ref: np.ndarray, dtype, what: str, lse: bool = Fa
     if lse:
         allowed = np.full_like(ref, LSE_TOL[dtype])
     else:
-        allowed = TOL[dtype] + (2.0 ** -9 * np.abs(ref) if dtype == torch.bfloat16 else 0.0)
+        # a bf16 output adds its own rounding: half an ulp, up to 2^-8 |o| for 8 significant bits
+        allowed = TOL[dtype] + (2.0 ** -8 * np.abs(ref) if dtype == torch.bfloat16 else 0.0)
     bad = ~(err <= allowed)  # NaN counts as bad
     if bad.any():
         i = np.unravel_index(np.argmax(np.where(bad, err, -1)), ref.shape)
