@@ -102,6 +102,9 @@ CASES = [
     ("mfma_all_pad", 1, 3, 32, 128, 50, 40, 32, "all", torch.bfloat16),
     ("mfma_out_of_range", 1, 4, 32, 128, 64, 40, 32, "oob", torch.bfloat16),
     ("mfma_decode_slices", 4, 1, 64, 128, 5000, 2048, 64, "some", torch.bfloat16),
+    # 4096 (query, 32 heads) tasks: the launch with a 2-tile ring per wave
+    ("mfma_many_d64", 1, 2048, 64, 64, 1000, 256, 64, "some", torch.bfloat16),
+    ("mfma_many_d128", 1, 4096, 32, 128, 2000, 160, 32, "oob", torch.bfloat16),
     ("valu_bk7", 2, 3, 32, 128, 200, 70, 7, "some", torch.bfloat16),
     ("valu_h16", 2, 3, 16, 64, 200, 70, 32, "some", torch.bfloat16),
     ("valu_fp32", 1, 6, 8, 64, 200, 64, 16, "some", torch.float32),

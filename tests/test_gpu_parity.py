@@ -196,25 +196,27 @@ def test_indexed_edge_cases(dev, spec, mode):
 
 
 MANY_TASKS = [
-    # name, B, M, H, N, K, pad pattern, splits: at head_dim 128, 4096 or more (query, 32 heads, slice)
-    # tasks take the kernel in which two 16-head waves share one ring; fewer take the deep-ring one.
-    ("many_some", 2, 2048, 32, 3000, 70, "some", 1),
-    ("many_oob_split", 1, 2048, 64, 3000, 100, "oob", 3),
-    ("many_pad_k33", 1, 4100, 32, 500, 33, "some", 1),
+    # name, B, M, H, D, N, K, pad pattern, splits: 4096 or more (query, 32 heads, slice) tasks take
+    # the launch with a 2-tile ring per wave; fewer take the 4-tile one.
+    ("many_some", 2, 2048, 32, 128, 3000, 70, "some", 1),
+    ("many_oob_split", 1, 2048, 64, 128, 3000, 100, "oob", 3),
+    ("many_pad_k33", 1, 4100, 32, 128, 500, 33, "some", 1),
+    ("many_d64", 1, 2048, 64, 64, 1000, 90, "some", 1),
+    ("many_d64_split", 1, 1024, 32, 64, 800, 200, "oob", 4),
 ]
 
 
 @pytest.mark.parametrize("spec", MANY_TASKS, ids=[c[0] for c in MANY_TASKS])
 @pytest.mark.parametrize("mode", [W.SINK_NONE, W.SINK_KEY0, W.SINK_NULL])
 def test_indexed_many_tasks(dev, spec, mode):
-    name, B, M, H, N, K, pattern, splits = spec
+    name, B, M, H, D, N, K, pattern, splits = spec
     rng = np.random.default_rng(13)
     idx = _edge_lists(rng, B, M, N, K, pattern)
     if mode == W.SINK_KEY0:
         sub = idx[:, ::5]
         sub[~(sub == 0).any(-1), 1] = 0  # row 0 in every fifth list, never twice
         idx[:, ::5] = sub
-    case = W.make_indexed_case(f"{name}_m{mode}", B, M, H, 128, N, idx, mode, seed=10, num_splits=splits)
+    case = W.make_indexed_case(f"{name}_m{mode}", B, M, H, D, N, idx, mode, seed=10, num_splits=splits)
     _log(case.name, check_indexed(case, dev))
 
 
