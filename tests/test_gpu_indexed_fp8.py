@@ -56,6 +56,8 @@ CASES = [
     (5, 2, 3, 32, 2000, 700, 64, 0, 2, 3),    # split-K: lists longer than a staged chunk
     (6, 3, 2, 32, 700, 129, 0, 1, 1, 4),
     (7, 1, 1, 32, 40, 33, 64, 33, 2, 1),      # every entry -1: o = 0, lse = sink
+    (8, 1, 4096, 32, 1500, 70, 0, 5, 1, 1),   # 4096 tasks: the 2-tile-ring launch, no rotary dims
+    (9, 1, 2048, 64, 1500, 100, 64, 0, 2, 2), # 8192 tasks with two slices, rotary dims
 ]
 
 
