@@ -171,6 +171,18 @@ def _check_dev(name, t, dev, dtype=None):
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+def _check_shape(name, t, shape):
+    """Sizes are checked before devices and dtypes: a too-small `out` or a short `sinks` would make the
+    kernels write or read past the allocation, since every extent they use comes from q."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _check_sinks(sinks, num_heads):
+    if sinks is not None and (sinks.dim() != 1 or sinks.numel() != num_heads):
+        raise ValueError(f"sinks must hold num_heads = {num_heads} values, got shape {tuple(sinks.shape)}")
+
+
 def _sink_mode(mode, sinks):
     m = SINK_MODES[mode] if isinstance(mode, str) else int(mode)
     if m != 0 and sinks is None:
@@ -189,13 +201,19 @@ def window_fwd(q, k, v, cu_seqlens, max_seqlen: int, *, window=(-1, -1), softmax
     dt = q.dtype
     if dt not in _DTYPES:
         raise ValueError(f"unsupported dtype {dt}")
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_dev(name, t, dev, dt)
-    _check_dev("cu_seqlens", cu_seqlens, dev, torch.int32)
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("q must be [T, H, D] and k, v [T, Hkv, D]")
     T, H, D = q.shape
     Hkv = k.shape[1]
     if k.shape != (T, Hkv, D) or v.shape != (T, Hkv, D):
         raise ValueError("k and v must be [T, Hkv, D] like q")
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-D tensor of num_seqs + 1 offsets")
+    _check_shape("out", out, q.shape)
+    _check_sinks(sinks, H)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(name, t, dev, dt)
+    _check_dev("cu_seqlens", cu_seqlens, dev, torch.int32)
     mode = _sink_mode(sink_mode, sinks)
     if sinks is not None:
         _check_dev("sinks", sinks, dev, torch.float32)
@@ -228,14 +246,18 @@ def indexed_fwd(q, kv, topk_idxs, *, softmax_scale: float | None = None, sinks=N
     dt = q.dtype
     if dt not in _DTYPES:
         raise ValueError(f"unsupported dtype {dt}")
-    _check_dev("q", q, dev, dt)
-    _check_dev("kv", kv, dev, dt)
-    _check_dev("topk_idxs", topk_idxs, dev, torch.int32)
+    if q.dim() != 4 or kv.dim() != 3 or topk_idxs.dim() != 3:
+        raise ValueError("q must be [B, M, H, D], kv [B, N, D] and topk_idxs [B, M, K]")
     B, M, H, D = q.shape
     N = kv.shape[1]
     K = topk_idxs.shape[2]
     if kv.shape != (B, N, D) or topk_idxs.shape[:2] != (B, M):
         raise ValueError("kv must be [B, N, D] and topk_idxs [B, M, K]")
+    _check_shape("out", out, q.shape)
+    _check_sinks(sinks, H)
+    _check_dev("q", q, dev, dt)
+    _check_dev("kv", kv, dev, dt)
+    _check_dev("topk_idxs", topk_idxs, dev, torch.int32)
     mode = _sink_mode(sink_mode, sinks)
     if sinks is not None:
         _check_dev("sinks", sinks, dev, torch.float32)
@@ -265,20 +287,24 @@ def indexed_fp8_fwd(q, kv_fp8, kv_scale, kv_rope, topk_idxs, *, softmax_scale: f
     kv_rope bf16 [B,N,rd] or None (rd = 0); topk_idxs int32 [B,M,K] (-1 = unused).
     """
     dev = q.device
+    if q.dim() != 4 or kv_fp8.dim() != 3 or topk_idxs.dim() != 3 or (kv_rope is not None and kv_rope.dim() != 3):
+        raise ValueError("q must be [B, M, H, D], kv_fp8 and kv_rope [B, N, .] and topk_idxs [B, M, K]")
+    B, M, H, D = q.shape
+    N = kv_fp8.shape[1]
+    rd = 0 if kv_rope is None else kv_rope.shape[2]
+    if kv_rope is not None and kv_rope.shape[:2] != (B, N):
+        raise ValueError("kv_rope must be [B, N, rope_dims]")
+    K = topk_idxs.shape[2]
+    if kv_fp8.shape != (B, N, D - rd) or kv_scale.shape != (B, N) or topk_idxs.shape[:2] != (B, M):
+        raise ValueError("kv_fp8 must be [B, N, D - rope_dims], kv_scale [B, N] and topk_idxs [B, M, K]")
+    _check_shape("out", out, q.shape)
+    _check_sinks(sinks, H)
     _check_dev("q", q, dev, torch.bfloat16)
     _check_dev("kv_fp8", kv_fp8, dev, torch.uint8)
     _check_dev("kv_scale", kv_scale, dev, torch.float32)
     _check_dev("topk_idxs", topk_idxs, dev, torch.int32)
-    B, M, H, D = q.shape
-    N = kv_fp8.shape[1]
-    rd = 0 if kv_rope is None else kv_rope.shape[2]
     if kv_rope is not None:
         _check_dev("kv_rope", kv_rope, dev, torch.bfloat16)
-        if kv_rope.shape[:2] != (B, N):
-            raise ValueError("kv_rope must be [B, N, rope_dims]")
-    K = topk_idxs.shape[2]
-    if kv_fp8.shape != (B, N, D - rd) or kv_scale.shape != (B, N) or topk_idxs.shape[:2] != (B, M):
-        raise ValueError("kv_fp8 must be [B, N, D - rope_dims], kv_scale [B, N] and topk_idxs [B, M, K]")
     mode = _sink_mode(sink_mode, sinks)
     if sinks is not None:
         _check_dev("sinks", sinks, dev, torch.float32)
@@ -305,11 +331,15 @@ def merge_lse(part_o, part_lse, *, sinks=None, sink_mode="none", out_dtype=torch
               return_lse: bool = False):
     """Merge partial (o_c, lse_c) results: part_o fp32 [S,R,H,D], part_lse fp32 [S,R,H]."""
     dev = part_o.device
-    _check_dev("part_o", part_o, dev, torch.float32)
-    _check_dev("part_lse", part_lse, dev, torch.float32)
+    if part_o.dim() != 4:
+        raise ValueError("part_o must be [S, R, H, D]")
     S, R, H, D = part_o.shape
     if part_lse.shape != (S, R, H):
         raise ValueError("part_lse must be [S, R, H]")
+    _check_shape("out", out, (R, H, D))
+    _check_sinks(sinks, H)
+    _check_dev("part_o", part_o, dev, torch.float32)
+    _check_dev("part_lse", part_lse, dev, torch.float32)
     mode = _sink_mode(sink_mode, sinks)
     if sinks is not None:
         _check_dev("sinks", sinks, dev, torch.float32)
@@ -359,10 +389,8 @@ def block_mass(q, kv, topk_idxs, lse, *, block_keys: int, softmax_scale: float |
     dt = q.dtype
     if dt not in _DTYPES:
         raise ValueError(f"unsupported dtype {dt}")
-    _check_dev("q", q, dev, dt)
-    _check_dev("kv", kv, dev, dt)
-    _check_dev("topk_idxs", topk_idxs, dev, torch.int32)
-    _check_dev("lse", lse, dev, torch.float32)
+    if q.dim() != 4 or kv.dim() != 3 or topk_idxs.dim() != 3:
+        raise ValueError("q must be [B, M, H, D], kv [B, N, D] and topk_idxs [B, M, K]")
     B, M, H, D = q.shape
     N = kv.shape[1]
     K = topk_idxs.shape[2]
@@ -370,6 +398,11 @@ def block_mass(q, kv, topk_idxs, lse, *, block_keys: int, softmax_scale: float |
         raise ValueError("kv must be [B, N, D], topk_idxs [B, M, K] and lse [B, M, H]")
     if block_keys < 1:
         raise ValueError("block_keys must be >= 1")
+    _check_sinks(sinks, H)
+    _check_dev("q", q, dev, dt)
+    _check_dev("kv", kv, dev, dt)
+    _check_dev("topk_idxs", topk_idxs, dev, torch.int32)
+    _check_dev("lse", lse, dev, torch.float32)
     mode = _sink_mode(sink_mode, sinks)
     if sinks is not None:
         _check_dev("sinks", sinks, dev, torch.float32)

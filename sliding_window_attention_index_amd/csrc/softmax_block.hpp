@@ -73,7 +73,10 @@ __device__ __forceinline__ bool softmax_need_rescale(RowSoftmax &rs, float bm, f
   const float m_new = fmaxf(rs.m, bm);
   const bool grow = (m_new - rs.m) * c > kRescaleLog2;  // -inf old max always grows when m_new is finite
   if (__ballot(grow)) {
-    alpha = fast_exp2((rs.m - m_new) * c);  // old -inf -> 0
+    // Old -inf -> 0.  A row that has still seen nothing (old and new max both -inf) keeps its
+    // state: its l and accumulator are 0 (or l = 1 for a null sink of -inf), and -inf - -inf
+    // would make the factor NaN.  Rows of one wave reach their first key at different blocks.
+    alpha = m_new == kNegInf ? 1.0f : fast_exp2((rs.m - m_new) * c);
     rs.l *= alpha;
     rs.m = m_new;
     return true;

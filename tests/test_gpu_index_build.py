@@ -18,8 +18,8 @@ pytestmark = pytest.mark.gpu
 
 @pytest.fixture(scope="module")
 def dev():
-    if not torch.cuda.is_available():
-        pytest.skip("no GPU")
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    sattn.load_library()  # fails loudly if the HIP library is missing
     return torch.device("cuda:0")
 
 

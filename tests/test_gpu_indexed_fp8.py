@@ -2,9 +2,10 @@
 
 Rows are e4m3 codes times a power-of-two scale per row on the first 128 - rope_dims dims and bf16
 on the last rope_dims.  Tolerances are those of the bf16 indexed path (the dequantised rows are
-exact in bf16): max-abs 1e-2 + 2^-9 |o| on the output, 2e-3 on the lse, for unit-normal rows as
+exact in bf16): max-abs 1e-2 + 2^-8 |o| on the output (the full-size prefill and decode shapes: 1e-2
+on the value before the output's rounding, tests/parity.py), 2e-3 on the lse, for unit-normal rows as
 there (the probabilities are rounded to bf16 before the PV product, an error of up to
-2^-9 sum_i p_i |v_i|, which that bound covers only when |v| stays near |o|).  Because the kernel turns
+2^-8 sum_i p_i |v_i|, which that bound covers only when |v| stays near |o|).  Because the kernel turns
 every fp8 value into the exact bf16 value before the products, its output must also equal, bit
 for bit, the bf16 kernel's over a bf16 cache holding the dequantised rows, when both place the same
 entries in the same tile rows.
@@ -18,7 +19,7 @@ import torch
 import sliding_window_attention_index_amd as sattn
 import workloads as W
 from oracle import fp8_cache as F8
-from parity import SINK_NAMES, compare, sample_rows
+from parity import SINK_NAMES, compare
 
 pytestmark = pytest.mark.gpu
 
@@ -95,29 +96,39 @@ def test_indexed_fp8_equals_bf16_kernel_on_dequantised_rows(dev, rd, mode, split
     assert torch.equal(o8.cpu(), o16.cpu()) and torch.equal(l8.cpu(), l16.cpu())
 
 
-def test_indexed_fp8_prefill_shape_sampled(dev):
-    """The prefill shape with an fp8 cache: 8192 queries x 32 heads, 8320 rows, 640-entry lists."""
+def _full_compare(o, lse, o_ref, l_ref, H, what):
+    e = compare(o.reshape(-1, H, 128), o_ref, torch.bfloat16, f"{what} o", literal=True)
+    compare(lse.reshape(-1, H), l_ref, torch.bfloat16, f"{what} lse", lse=True)
+    return e
+
+
+def test_indexed_fp8_prefill_shape_full(dev):
+    """The prefill shape with an fp8 cache as the bench times it (rd = 64): 8192 queries x 32 heads,
+    8320 rows, 640-entry lists; every element of o and lse."""
     c = W.sparse_prefill_case(seed=0)
     kv8, sc, rope = W.fp8_cache(3, 1, c.kv.shape[1], 128, 64, scale_spread=0)
     o, lse = sattn.indexed_fp8_fwd(c.q.to(dev), kv8.to(dev), sc.to(dev), rope.to(dev), c.topk_idxs.to(dev),
                                    softmax_scale=c.scale, return_lse=True)
     torch.cuda.synchronize(dev)
-    rows = sample_rows(c.q.shape[0] * c.q.shape[1], 48, seed=0, must=(0, 8191))
-    o_ref, l_ref = F8.indexed_fp8(c.q, kv8, sc, rope, c.topk_idxs, softmax_scale=c.scale, rows=rows)
-    e = compare(o.reshape(-1, 32, 128)[torch.from_numpy(rows)], o_ref, torch.bfloat16, "fp8 prefill o")
-    compare(lse.reshape(-1, 32)[torch.from_numpy(rows)], l_ref, torch.bfloat16, "fp8 prefill lse", lse=True)
-    print(f"[parity] indexed_fp8 prefill shape sampled: max_abs {e:.3e}", flush=True)
+    o, lse = o.cpu(), lse.cpu()
+    e = 0.0
+    for r0 in range(0, 8192, 2048):
+        rows = np.arange(r0, r0 + 2048)
+        o_ref, l_ref = F8.indexed_fp8(c.q, kv8, sc, rope, c.topk_idxs, softmax_scale=c.scale, rows=rows)
+        e = max(e, _full_compare(o[0, r0:r0 + 2048], lse[0, r0:r0 + 2048], o_ref, l_ref, 32, f"fp8 prefill rows {r0}.."))
+    print(f"[parity] indexed_fp8 prefill shape, all rows: max_abs {e:.3e}", flush=True)
 
 
-def test_indexed_fp8_decode_shape_split(dev):
-    """The decode shape with an fp8 cache: 64 rows x 64 heads, 32896-row caches, 2048 entries, 8 splits."""
+@pytest.mark.parametrize("rd", [64, 0])
+def test_indexed_fp8_decode_shape_split_full(dev, rd):
+    """The decode shape with an fp8 cache: 64 rows x 64 heads, 32896-row caches, 2048 entries, 8 splits
+    (rd = 64 is the benched layout); every element of o and lse."""
     c = W.sparse_decode_case(seed=0)
-    kv8, sc, rope = W.fp8_cache(4, 64, c.kv.shape[1], 128, 0, scale_spread=0)
-    o, lse = sattn.indexed_fp8_fwd(c.q.to(dev), kv8.to(dev), sc.to(dev), None, c.topk_idxs.to(dev),
+    kv8, sc, rope = W.fp8_cache(4, 64, c.kv.shape[1], 128, rd, scale_spread=0)
+    rope_d = rope.to(dev) if rd else None
+    o, lse = sattn.indexed_fp8_fwd(c.q.to(dev), kv8.to(dev), sc.to(dev), rope_d, c.topk_idxs.to(dev),
                                    softmax_scale=c.scale, num_splits=8, return_lse=True)
     torch.cuda.synchronize(dev)
-    rows = np.array([0, 17, 42, 63])
-    o_ref, l_ref = F8.indexed_fp8(c.q, kv8, sc, None, c.topk_idxs, softmax_scale=c.scale, rows=rows)
-    e = compare(o.reshape(-1, 64, 128)[torch.from_numpy(rows)], o_ref, torch.bfloat16, "fp8 decode o")
-    compare(lse.reshape(-1, 64)[torch.from_numpy(rows)], l_ref, torch.bfloat16, "fp8 decode lse", lse=True)
-    print(f"[parity] indexed_fp8 decode shape, 8 splits: max_abs {e:.3e}", flush=True)
+    o_ref, l_ref = F8.indexed_fp8(c.q, kv8, sc, rope if rd else None, c.topk_idxs, softmax_scale=c.scale)
+    e = _full_compare(o.cpu(), lse.cpu(), o_ref, l_ref, 64, f"fp8 decode rd={rd}")
+    print(f"[parity] indexed_fp8 decode shape rd={rd}, 8 splits, all rows: max_abs {e:.3e}", flush=True)

@@ -1,11 +1,14 @@
 """GPU parity: libsattn (through its C ABI) against the CPU oracle, element by element.
 
-Reduced versions of the five workloads are compared on every output element;
-the full-size workloads, launched exactly as bench.py times them, are compared
-on sampled query rows the oracle evaluates one by one.  Edge cases cover what
-the pages flag as risks: windows narrower than a key block, tiles that start
-at a sequence boundary (key-0 placement), length-1 and empty sequences,
-all-padding index lists, split counts that leave empty slices, and a
+Reduced versions of the five workloads and the full-size workloads, launched
+exactly as bench.py times them, are compared on every output element (the
+full-size ones in chunks of query rows, so the fp64 reference stays bounded).
+The fp32 split-K partials, which carry no output rounding, are compared with
+the oracle run on each slice alone at the bare max-abs 1e-2.  Edge cases cover
+what the pages flag as risks: windows narrower than a key block, tiles that
+start at a sequence boundary (key-0 placement), bands clipped at key 0 so that
+rows of one tile reach their first key in different blocks, length-1 and empty
+sequences, all-padding index lists, split counts that leave empty slices, and a
 non-default stream fed through an event.
 """
 import math
@@ -17,8 +20,8 @@ import torch
 import oracle
 import sliding_window_attention_index_amd as sattn
 import workloads as W
-from parity import (check_indexed, check_window, compare, oracle_indexed, oracle_window, run_indexed, run_window,
-                    sample_rows)
+from parity import (check_indexed, check_indexed_full, check_window, check_window_full, compare, oracle_indexed,
+                    oracle_window, run_indexed, run_window, split_slices, workspace_partials)
 
 pytestmark = pytest.mark.gpu
 
@@ -102,22 +105,40 @@ def test_window_max_seqlen_bounds_work(dev):
     assert torch.all(o[40:64] == 7.0)
 
 
-def test_vision_window_full_size_sampled(dev):
-    """16 sequences, lengths U[1024,4096], 16/8 heads, D=128, window +-128, key-0 sinks (bench workload)."""
-    case = W.vision_window()
-    cu = case.cu_seqlens.numpy()
-    must = list(cu[:-1]) + list(cu[1:] - 1) + list(cu[:-1] + 63) + list(cu[:-1] + 64) + list(cu[:-1] + 200)
-    rows = sample_rows(int(cu[-1]), 192, seed=1, must=must)
-    _log("vision_window full (sampled)", check_window(case, dev, rows=rows))
+def test_vision_window_full_size(dev):
+    """16 sequences, lengths U[1024,4096], 16/8 heads, D=128, window +-128, key-0 sinks (bench workload):
+    every element of o and lse."""
+    _log("vision_window full", check_window_full(W.vision_window(), dev))
 
 
-def test_causal_window_full_size_sampled(dev):
-    """4 x 8192 tokens, 64/8 heads, D=64, causal 128-key window, null sinks."""
-    case = W.causal_window_null()
-    cu = case.cu_seqlens.numpy()
-    must = list(cu[:-1]) + list(cu[1:] - 1) + list(cu[:-1] + 127) + list(cu[:-1] + 128)
-    rows = sample_rows(int(cu[-1]), 160, seed=2, must=must)
-    _log("causal_window_null full (sampled)", check_window(case, dev, rows=rows))
+def test_causal_window_full_size(dev):
+    """4 x 8192 tokens, 64/8 heads, D=64, causal 128-key window, null sinks: every element of o and lse."""
+    _log("causal_window_null full", check_window_full(W.causal_window_null(), dev))
+
+
+# Bands clipped at key 0 inside a tile: rows of one wave see their first key in different key blocks,
+# so a block can be empty for some rows while the running max of others grows.
+CLIPPED = [
+    # name, lens, H, Hkv, D, (wl, wr)
+    ("clip_g1_w40", [130, 65], 4, 4, 128, (40, 40)),
+    ("clip_g2_w20", [64, 300], 4, 2, 128, (20, 20)),
+    ("clip_g1_d64_w40", [200, 33], 4, 4, 64, (40, 40)),
+    ("clip_g4_d64_w9", [150, 70], 8, 2, 64, (9, 3)),
+]
+
+
+CLIPPED_MODES = [(W.SINK_NONE, False), (W.SINK_KEY0, False), (W.SINK_NULL, False), (W.SINK_KEY0, True),
+                 (W.SINK_NULL, True)]
+
+
+@pytest.mark.parametrize("spec", CLIPPED, ids=[c[0] for c in CLIPPED])
+@pytest.mark.parametrize("mode,neg_inf_sinks", CLIPPED_MODES, ids=["none", "key0", "null", "key0_neginf", "null_neginf"])
+def test_window_clipped_band(dev, spec, mode, neg_inf_sinks):
+    name, lens, H, Hkv, D, (wl, wr) = spec
+    case = W.make_window_case(f"{name}_m{mode}", lens, H, Hkv, D, wl, wr, mode, seed=21)
+    if neg_inf_sinks:
+        case.sinks[::2] = -math.inf  # every other head: a key-0 logit of -inf, or a null sink that adds nothing
+    _log(case.name + ("_neginf" if neg_inf_sinks else ""), check_window(case, dev))
 
 
 # ---------------------------------------------------------------------------
@@ -229,18 +250,62 @@ def test_indexed_padding_bit_exact(dev):
     assert torch.equal(o0, o1)
 
 
-def test_sparse_prefill_full_size_sampled(dev):
-    """8192 queries x 32 heads x 640 listed rows of a 8320-row shared cache (as timed by the bench)."""
-    case = W.sparse_prefill_case()
-    rows = sample_rows(case.q.shape[1], 128, seed=3, must=[0, 1, 8191])
-    _log("sparse_prefill full (sampled)", check_indexed(case, dev, rows=rows))
+def test_sparse_prefill_full_size(dev):
+    """8192 queries x 32 heads x 640 listed rows of a 8320-row shared cache (as timed by the bench):
+    every element of o and lse."""
+    _log("sparse_prefill full", check_indexed_full(W.sparse_prefill_case(), dev))
 
 
-def test_sparse_decode_full_size_sampled(dev):
-    """64 decode queries x 64 heads, 2048-entry lists over 32896-row caches, 8 splits + merge."""
+def test_sparse_decode_full_size(dev):
+    """64 decode queries x 64 heads, 2048-entry lists over 32896-row caches, 8 splits + merge (as timed
+    by the bench): every element of o and lse."""
+    _log("sparse_decode full", check_indexed_full(W.sparse_decode_case(), dev))
+
+
+def _check_partials(case, dev, num_splits):
+    """Each slice's fp32 partial (o_c, lse_c), read from the workspace after the call, against the oracle
+    over that slice of the lists alone (no null sink: it enters in the merge), at the bare max-abs 1e-2
+    on o_c (no output rounding) and 2e-3 on lse_c."""
+    B, M, H, D, N, K = case.dims
+    ws = torch.empty(sattn.indexed_workspace_size(B, M, H, D, num_splits), dtype=torch.uint8, device=dev)
+    q, kv, idx = case.q.to(dev), case.kv.to(dev), case.topk_idxs.to(dev)
+    sinks = case.sinks.to(dev) if case.sinks is not None else None
+    o = sattn.indexed_fwd(q, kv, idx, softmax_scale=case.scale, sinks=sinks,
+                          sink_mode=("none", "key0", "null")[case.sink_mode], num_splits=num_splits, workspace=ws)
+    torch.cuda.synchronize(dev)
+    slices = split_slices(K, num_splits)
+    po, pl = (t.cpu() for t in workspace_partials(ws, num_splits, B * M, H, D, len(slices)))
+    worst = 0.0
+    for c, (a, b) in enumerate(slices):
+        ro, rl = oracle.indexed(case.q, case.kv, case.topk_idxs[:, :, a:b].contiguous(), scale=case.scale,
+                                sinks=case.sinks, sink_mode=W.SINK_KEY0 if case.sink_mode == W.SINK_KEY0 else W.SINK_NONE)
+        worst = max(worst, compare(po[c], ro, case.q.dtype, f"{case.name} part_o[{c}]", tol=1e-2))
+        compare(pl[c], rl, case.q.dtype, f"{case.name} part_lse[{c}]", lse=True)
+    return {"max_abs_part_o": worst, "parts": len(slices), "o": o}
+
+
+def test_sparse_prefill_split_partials_literal_bar(dev):
+    """The prefill workload cut into 4 slices of 160 entries (ragged 32-entry blocks)."""
+    r = _check_partials(W.sparse_prefill_case(), dev, 4)
+    _log("sparse_prefill partials", {k: v for k, v in r.items() if k != "o"})
+
+
+def test_sparse_decode_split_partials_literal_bar(dev):
+    """The decode workload's own 8 slices of 256 entries."""
     case = W.sparse_decode_case()
-    rows = sample_rows(64, 24, seed=4, must=[0, 63])
-    _log("sparse_decode full (sampled)", check_indexed(case, dev, rows=rows))
+    r = _check_partials(case, dev, case.num_splits)
+    _log("sparse_decode partials", {k: v for k, v in r.items() if k != "o"})
+
+
+@pytest.mark.parametrize("mode", [W.SINK_NONE, W.SINK_KEY0, W.SINK_NULL])
+@pytest.mark.parametrize("splits", [3, 8])
+def test_split_partials_reduced(dev, mode, splits):
+    case = W.sparse_decode_case(batch=4, total_tokens=8192, n_pick=480, num_splits=splits, sink_mode=mode,
+                                name=f"partials_s{splits}_m{mode}")
+    # the decoded position is a multiple of the ring size, so ring slot 0 (cache row 0) is in every list
+    assert bool((case.topk_idxs == 0).any(-1).all())
+    r = _check_partials(case, dev, splits)
+    _log(case.name, {k: v for k, v in r.items() if k != "o"})
 
 
 # ---------------------------------------------------------------------------
@@ -263,6 +328,8 @@ def test_merge_lse_parity(dev, mode, out_dtype):
     ro, rl = oracle.merge(po, pl, sinks=sinks, sink_mode=mode)
     compare(o.cpu(), ro, out_dtype, "merge o")
     compare(lse.cpu(), rl, torch.float32, "merge lse", lse=True)
+    if out_dtype == torch.float32:  # no output rounding: the literal bar of bf16-input work as well
+        compare(o.cpu(), ro, torch.float32, "merge o (fp32 out)", tol=1e-2)
 
 
 def test_non_default_stream_with_event(dev):
