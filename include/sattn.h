@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define SATTN_ABI_VERSION 6
+#define SATTN_ABI_VERSION 7
 
 typedef enum {
   SATTN_OK = 0,
@@ -66,7 +66,9 @@ typedef enum {
   SATTN_ERR_ALIGNMENT = 5,   /* a tensor pointer is not 16-byte aligned           */
   SATTN_ERR_WORKSPACE = 6,   /* split-K workspace missing or too small            */
   SATTN_ERR_LAUNCH = 7,      /* the HIP runtime rejected a kernel launch          */
-  SATTN_ERR_ARG = 8          /* bad enum value or option                          */
+  SATTN_ERR_ARG = 8,         /* bad enum value or option                          */
+  SATTN_ERR_SCRATCH_LIMIT = 9 /* split-K partials exceed the fixed scratch of
+                                 sattn_indexed_fwd_noalloc                          */
 } sattn_status;
 
 typedef enum { SATTN_BF16 = 0, SATTN_F32 = 1 } sattn_dtype;
@@ -404,6 +406,24 @@ sattn_status sattn_indexed_fp8_fwd(const sattn_indexed_fp8_args *args, hipStream
 sattn_status sattn_window_fwd(const sattn_window_args *args, hipStream_t stream);
 sattn_status sattn_indexed_fwd(const sattn_indexed_args *args, hipStream_t stream);
 sattn_status sattn_merge_lse(const sattn_merge_args *args, hipStream_t stream);
+
+/*
+ * sattn_indexed_fwd for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments, kernels and
+ * results; `workspace` and `workspace_bytes` are ignored and the split-K partials (num_splits > 1)
+ * go to a fixed scratch array of SATTN_NOALLOC_SCRATCH_BYTES that the library holds on every GPU
+ * it has run on until the process ends.  The call allocates nothing.
+ *   - Calls whose partials need more than the scratch
+ *     (sattn_indexed_workspace_size(...) > SATTN_NOALLOC_SCRATCH_BYTES) return
+ *     SATTN_ERR_SCRATCH_LIMIT before anything is enqueued.
+ *   - The scratch of the current device (hipGetDevice) is used; `stream` must belong to it.
+ *   - Every call on one GPU shares that GPU's scratch: calls that overlap on one GPU (on
+ *     different streams, or from several host threads without ordering) race and give wrong
+ *     results.  Calls ordered on one stream do not.
+ *   - With num_splits == 1 no scratch is touched.
+ */
+#define SATTN_NOALLOC_SCRATCH_BYTES (32u << 20)
+sattn_status sattn_indexed_fwd_noalloc(const sattn_indexed_args *args, hipStream_t stream);
 
 /* Bytes of split-K workspace sattn_indexed_fwd needs (0 when num_splits <= 1). */
 size_t sattn_indexed_workspace_size(int32_t batch, int32_t q_len, int32_t num_heads,

@@ -22,7 +22,7 @@ import os
 
 import torch  # loads the HIP runtime libsattn links against
 
-__all__ = ["window_fwd", "indexed_fwd", "indexed_fp8_fwd", "merge_lse", "build_topk_idxs", "block_mass", "compress_pool", "indexer_topk",
+__all__ = ["window_fwd", "indexed_fwd", "indexed_fwd_noalloc", "indexed_fp8_fwd", "merge_lse", "build_topk_idxs", "block_mass", "compress_pool", "indexer_topk",
            "indexed_workspace_size",
            "SattnError",
            "library_path", "load_library", "abi_version", "SINK_MODES"]
@@ -122,6 +122,8 @@ def load_library(path: str | None = None):
     lib.sattn_window_fwd.restype = ctypes.c_int
     lib.sattn_indexed_fwd.argtypes = [ctypes.POINTER(_IndexedArgs), P]
     lib.sattn_indexed_fwd.restype = ctypes.c_int
+    lib.sattn_indexed_fwd_noalloc.argtypes = [ctypes.POINTER(_IndexedArgs), P]
+    lib.sattn_indexed_fwd_noalloc.restype = ctypes.c_int
     lib.sattn_merge_lse.argtypes = [ctypes.POINTER(_MergeArgs), P]
     lib.sattn_merge_lse.restype = ctypes.c_int
     lib.sattn_build_topk_idxs.argtypes = [ctypes.POINTER(_BuildIdxArgs), P]
@@ -277,6 +279,44 @@ def indexed_fwd(q, kv, topk_idxs, *, softmax_scale: float | None = None, sinks=N
     if st != 0:
         raise SattnError(st, "sattn_indexed_fwd")
     return (o, lse) if return_lse else o
+
+
+def indexed_fwd_noalloc(q, kv, topk_idxs, *, out, lse=None, softmax_scale: float | None = None, sinks=None,
+                        sink_mode="none", num_splits: int = 1):
+    """indexed_fwd through sattn_indexed_fwd_noalloc: nothing is allocated, here or in the library
+    (usable under graph capture).  The caller passes `out` [B,M,H,D] and, if wanted, `lse` fp32
+    [B,M,H]; split-K partials go to the library's fixed per-GPU scratch
+    (SATTN_NOALLOC_SCRATCH_BYTES), so calls that overlap on one GPU race.  Returns `out`."""
+    dev = q.device
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    if q.dim() != 4 or kv.dim() != 3 or topk_idxs.dim() != 3:
+        raise ValueError("q must be [B, M, H, D], kv [B, N, D] and topk_idxs [B, M, K]")
+    B, M, H, D = q.shape
+    N = kv.shape[1]
+    K = topk_idxs.shape[2]
+    if kv.shape != (B, N, D) or topk_idxs.shape[:2] != (B, M):
+        raise ValueError("kv must be [B, N, D] and topk_idxs [B, M, K]")
+    _check_shape("out", out, q.shape)
+    _check_shape("lse", lse, (B, M, H))
+    _check_sinks(sinks, H)
+    _check_dev("q", q, dev, dt)
+    _check_dev("kv", kv, dev, dt)
+    _check_dev("topk_idxs", topk_idxs, dev, torch.int32)
+    _check_dev("out", out, dev, dt)
+    if lse is not None:
+        _check_dev("lse", lse, dev, torch.float32)
+    mode = _sink_mode(sink_mode, sinks)
+    if sinks is not None:
+        _check_dev("sinks", sinks, dev, torch.float32)
+    a = _IndexedArgs(_DTYPES[dt], _ptr(q), _ptr(kv), _ptr(topk_idxs), _ptr(out), _ptr(lse), B, M, H, D, N, K,
+                     float(1.0 / math.sqrt(D) if softmax_scale is None else softmax_scale),
+                     _ptr(sinks) if mode else None, mode, int(num_splits), None, 0)
+    st = _lib_handle().sattn_indexed_fwd_noalloc(ctypes.byref(a), _stream(dev))
+    if st != 0:
+        raise SattnError(st, "sattn_indexed_fwd_noalloc")
+    return out
 
 
 def indexed_fp8_fwd(q, kv_fp8, kv_scale, kv_rope, topk_idxs, *, softmax_scale: float | None = None, sinks=None,

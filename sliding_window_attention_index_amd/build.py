@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libsattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["sattn_api.cpp", "valu_fwd.hip", "indexed_mfma.hip", "indexed_fp8.hip", "window_mfma.hip", "index_build.hip",
+SOURCES = ["sattn_api.cpp", "sattn_noalloc.hip", "valu_fwd.hip", "indexed_mfma.hip", "indexed_fp8.hip", "window_mfma.hip", "index_build.hip",
            "compress.hip", "indexer.hip"]
 HEADERS = ["sattn_device.hpp", "sattn_kernels.hpp", "softmax_block.hpp", "lds_tile.hpp"]
 # MFMA kernels keep their accumulators in VGPRs: the online-softmax rescale is a VALU

@@ -59,6 +59,7 @@ const char *sattn_status_string(sattn_status s) {
     case SATTN_ERR_WORKSPACE: return "split-K workspace missing, misaligned or too small";
     case SATTN_ERR_LAUNCH: return "kernel launch failed";
     case SATTN_ERR_ARG: return "invalid enum value or option";
+    case SATTN_ERR_SCRATCH_LIMIT: return "split-K partials larger than the library's fixed scratch";
   }
   return "unknown status";
 }
@@ -156,7 +157,15 @@ sattn_status sattn_merge_lse(const sattn_merge_args *a, hipStream_t stream) {
   return launch_status(sattn::launch_merge(p, stream));
 }
 
-sattn_status sattn_indexed_fwd(const sattn_indexed_args *a, hipStream_t stream) {
+}  // extern "C"
+
+namespace sattn {
+
+// sattn_indexed_fwd with the split-K workspace given separately (the caller's buffer, or the
+// library's fixed scratch for sattn_indexed_fwd_noalloc); a->workspace and a->workspace_bytes are
+// not read here.
+sattn_status indexed_fwd_with_workspace(const sattn_indexed_args *a, void *workspace, size_t workspace_bytes,
+                                        hipStream_t stream) {
   if (!a) return SATTN_ERR_NULL_PTR;
   if (!valid_dtype(a->dtype)) return SATTN_ERR_DTYPE;
   if (!valid_sink(a->sink_mode)) return SATTN_ERR_ARG;
@@ -198,7 +207,7 @@ sattn_status sattn_indexed_fwd(const sattn_indexed_args *a, hipStream_t stream) 
   int parts = 1;
   if (a->num_splits > 1) {
     const size_t need = sattn_indexed_workspace_size(a->batch, a->q_len, a->num_heads, a->head_dim, a->num_splits);
-    if (!a->workspace || (reinterpret_cast<uintptr_t>(a->workspace) & 255u) || a->workspace_bytes < need)
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) || workspace_bytes < need)
       return SATTN_ERR_WORKSPACE;
     p.part_len = (a->topk + a->num_splits - 1) / a->num_splits;
     parts = (a->topk + p.part_len - 1) / p.part_len;  // slices that hold at least one entry
@@ -210,7 +219,7 @@ sattn_status sattn_indexed_fwd(const sattn_indexed_args *a, hipStream_t stream) 
     if (mfma && sattn::indexed_mfma_supported(p)) return launch_status(sattn::launch_indexed_mfma(p, stream));
     return launch_status(sattn::launch_indexed_valu(p, elem, stream));
   }
-  char *ws = static_cast<char *>(a->workspace);
+  char *ws = static_cast<char *>(workspace);
   p.num_parts = parts;
   p.part_o = reinterpret_cast<float *>(ws);
   p.part_lse = reinterpret_cast<float *>(ws + part_o_bytes(a->num_splits, rows, a->num_heads, a->head_dim));
@@ -230,6 +239,15 @@ sattn_status sattn_indexed_fwd(const sattn_indexed_args *a, hipStream_t stream) 
   m.o = a->o;
   m.lse = a->lse;
   return launch_status(sattn::launch_merge(m, stream));
+}
+
+}  // namespace sattn
+
+extern "C" {
+
+sattn_status sattn_indexed_fwd(const sattn_indexed_args *a, hipStream_t stream) {
+  if (!a) return SATTN_ERR_NULL_PTR;
+  return sattn::indexed_fwd_with_workspace(a, a->workspace, a->workspace_bytes, stream);
 }
 
 sattn_status sattn_block_mass(const sattn_block_mass_args *a, hipStream_t stream) {

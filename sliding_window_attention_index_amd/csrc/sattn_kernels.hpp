@@ -107,3 +107,11 @@ bool block_mass_mfma_supported(const IndexedParams &p);
 hipError_t launch_block_mass_mfma(const IndexedParams &p, hipStream_t stream);
 
 }  // namespace sattn
+
+#include "sattn.h"
+
+namespace sattn {
+// The C ABI's indexed call with the split-K workspace given separately (sattn_api.cpp).
+sattn_status indexed_fwd_with_workspace(const sattn_indexed_args *a, void *workspace, size_t workspace_bytes,
+                                        hipStream_t stream);
+}  // namespace sattn

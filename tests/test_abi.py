@@ -17,7 +17,7 @@ from sliding_window_attention_index_amd import (_BlockMassArgs, _BuildIdxArgs, _
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sattn.h")
 
-OK, NULL_PTR, SHAPE, DTYPE, UNSUPPORTED, ALIGNMENT, WORKSPACE, LAUNCH, ARG = range(9)
+OK, NULL_PTR, SHAPE, DTYPE, UNSUPPORTED, ALIGNMENT, WORKSPACE, LAUNCH, ARG, SCRATCH_LIMIT = range(10)
 
 
 @pytest.fixture(scope="module")
@@ -36,7 +36,8 @@ def _declared_functions():
 
 def test_header_functions_exported(lib):
     names = _declared_functions()
-    assert set(names) == {"sattn_window_fwd", "sattn_indexed_fwd", "sattn_merge_lse", "sattn_build_topk_idxs",
+    assert set(names) == {"sattn_window_fwd", "sattn_indexed_fwd", "sattn_indexed_fwd_noalloc", "sattn_merge_lse",
+                          "sattn_build_topk_idxs",
                           "sattn_block_mass", "sattn_compress_pool", "sattn_indexer_topk", "sattn_indexed_fp8_fwd",
                           "sattn_indexed_workspace_size", "sattn_status_string", "sattn_abi_version"}
     for name in names:
@@ -47,11 +48,11 @@ def test_abi_version_and_status_strings(lib):
     m = re.search(r"#define SATTN_ABI_VERSION (\d+)", open(HEADER).read())
     assert lib.sattn_abi_version() == int(m.group(1))
     seen = set()
-    for s in range(9):
+    for s in range(10):
         txt = lib.sattn_status_string(s).decode()
         assert txt and txt != "unknown status"
         seen.add(txt)
-    assert len(seen) == 9
+    assert len(seen) == 10
     assert lib.sattn_status_string(99).decode() == "unknown status"
 
 
@@ -311,3 +312,17 @@ def test_indexed_fp8_validation(lib, kw, status):
 def test_indexed_fp8_empty_is_noop(lib):
     assert lib.sattn_indexed_fp8_fwd(ctypes.byref(_f8(batch=0, q=None)), None) == OK
     assert lib.sattn_indexed_fp8_fwd(None, None) == NULL_PTR
+
+
+def test_indexed_noalloc_scratch_limit(lib):
+    """Split-K partials beyond SATTN_NOALLOC_SCRATCH_BYTES are refused before the device is touched."""
+    m = re.search(r"#define SATTN_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+    limit = int(m.group(1)) << int(m.group(2))
+    fake = 1 << 20  # never dereferenced: the call returns before any launch
+    B, M, H, D, S = 64, 1, 64, 128, 8
+    assert lib.sattn_indexed_workspace_size(B, M, H, D, S) <= limit
+    big = 2 * B  # twice the rows: twice the partials
+    assert lib.sattn_indexed_workspace_size(big, M, H, D, S) > limit
+    a = _IndexedArgs(0, fake, fake, fake, fake, None, big, M, H, D, 4096, 2048, 0.088, None, 0, S, None, 0)
+    assert lib.sattn_indexed_fwd_noalloc(ctypes.byref(a), None) == SCRATCH_LIMIT
+    assert lib.sattn_indexed_fwd_noalloc(None, None) == NULL_PTR
