@@ -348,25 +348,43 @@ def _reseed_window(case, s):
 
 
 def time_workload(wl, steps, warmup):
-    """Wall time of `steps` launches (synchronised on both sides) and the mean per-launch event time."""
+    """Wall time of exactly `steps` launches (synchronised on both sides) and the mean per-launch
+    event time.
+
+    The launches are captured once into a HIP graph of `group` consecutive launches (the largest
+    divisor of `steps` up to 16; the input sets rotate as eager calls would rotate them) and the graph
+    is replayed steps / group times: a launch of a few microseconds is shorter than the host's own
+    per-call overhead, and eager back-to-back calls would time the host.  Events on the replay
+    stream bracket every replay; per-launch time = replay time / group.
+    """
     import torch
+    group = max(g for g in range(1, 17) if steps % g == 0)
     for i in range(warmup):
         wl.launch(i)
     torch.cuda.synchronize()
-    # per-launch durations from events on the launch stream (torch's current stream)
-    stream = torch.cuda.current_stream()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(graph, stream=cap):
+        for i in range(group):
+            wl.launch(i)
     torch.cuda.synchronize()
+    replays = steps // group
+    for _ in range(2):  # warm replays
+        graph.replay()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(replays)]
+    stream = torch.cuda.current_stream()
     t0 = time.perf_counter()
-    for i in range(steps):
+    for i in range(replays):
         evs[i][0].record(stream)
-        wl.launch(i)
+        graph.replay()
         evs[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ev_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    ev_ms = sorted(a.elapsed_time(b) / group for a, b in evs)
     mean_ev = sum(ev_ms) / len(ev_ms)
-    return wall, mean_ev, ev_ms[len(ev_ms) // 2]
+    return wall, mean_ev, ev_ms[len(ev_ms) // 2], replays * group
 
 
 def roofline(wl, kernel_ms):
@@ -488,7 +506,7 @@ def main():
         print(f"[bench] preparing {name}", file=sys.stderr, flush=True)
         wl = build_workload(name, dev)
         steps = args.steps
-        wall, mean_ev, med_ev = time_workload(wl, steps, args.warmup)
+        wall, mean_ev, med_ev, launched = time_workload(wl, steps, args.warmup)
         ms = wall / steps * 1e3
         rec = {"value": round(wl.pairs / (ms / 1e3), 1), "unit": wl.unit, "ms_per_step": round(ms, 5),
                "kernel_ms_mean": round(mean_ev, 5), "kernel_ms_median": round(med_ev, 5), "pairs": wl.pairs,

@@ -134,14 +134,19 @@ typedef struct {
  *   o         [batch, q_len, num_heads, head_dim]  dtype (written)
  *   lse       [batch, q_len, num_heads] fp32 natural log (written; may be NULL)
  *   num_splits 1: one pass.  S > 1: the list is cut into S contiguous slices
- *             of ceil(topk / S) entries; each slice's normalised partial
- *             output and log-sum-exp go to `workspace`, then a second kernel
- *             on the same stream merges them (sattn_merge_lse) into o / lse.
- *             A null sink enters once, in the merge; a key-0 bias applies in
- *             the slice that holds row 0.  1 <= S <= topk is required.
+ *             of ceil(topk / S) entries (slices that would hold no entry are
+ *             not created); each slice's normalised partial output and
+ *             log-sum-exp go to `workspace`, then a second kernel on the same
+ *             stream merges them (sattn_merge_lse) into o / lse.  A null sink
+ *             enters once, in the merge; a key-0 bias applies in the slice that
+ *             holds row 0.  1 <= S <= topk is required.
  *   workspace  device buffer of at least
  *             sattn_indexed_workspace_size(batch, q_len, num_heads, head_dim, S)
- *             bytes, 256-byte aligned (may be NULL when S == 1).
+ *             bytes, 256-byte aligned (may be NULL when S == 1).  Layout:
+ *             part_o [S, batch*q_len, num_heads, head_dim] fp32, then part_lse
+ *             [S, batch*q_len, num_heads] fp32, each from a 256-byte boundary;
+ *             after the call the slices' partials are there.  Calls that overlap
+ *             and share one workspace race.
  */
 typedef struct {
   sattn_dtype dtype;

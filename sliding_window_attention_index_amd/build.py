@@ -22,13 +22,14 @@ LIB = os.path.join(PKG, "libsattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["sattn_api.cpp", "sattn_noalloc.hip", "valu_fwd.hip", "indexed_mfma.hip", "indexed_fp8.hip", "window_mfma.hip", "index_build.hip",
+SOURCES = ["sattn_api.cpp", "sattn_noalloc.hip", "valu_fwd.hip", "indexed_mfma.hip", "indexed_slice.hip", "indexed_fp8.hip", "window_mfma.hip", "index_build.hip",
            "compress.hip", "indexer.hip"]
 HEADERS = ["sattn_device.hpp", "sattn_kernels.hpp", "softmax_block.hpp", "lds_tile.hpp"]
 # MFMA kernels keep their accumulators in VGPRs: the online-softmax rescale is a VALU
 # multiply, which cannot read AGPRs and would otherwise copy the accumulator every block.
 EXTRA_FLAGS = {
     "indexed_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "indexed_slice.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "indexed_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "window_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
@@ -37,7 +38,7 @@ EXTRA_FLAGS = {
 # not spill: a compiler-inserted scratch access is one more vector-memory operation in flight and
 # would make those waits return early.  The build reads the compiler's resource report for these
 # sources and fails on any scratch use.
-NO_SCRATCH = {"indexed_mfma.hip", "indexed_fp8.hip", "window_mfma.hip", "indexer.hip"}
+NO_SCRATCH = {"indexed_mfma.hip", "indexed_slice.hip", "indexed_fp8.hip", "window_mfma.hip", "indexer.hip"}
 _USAGE = "kernel-resource-usage"
 
 COMMON_FLAGS = [

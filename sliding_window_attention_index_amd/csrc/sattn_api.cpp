@@ -214,8 +214,12 @@ sattn_status indexed_fwd_with_workspace(const sattn_indexed_args *a, void *works
   }
   const int elem = a->dtype == SATTN_F32 ? sattn::kF32 : sattn::kBF16;
   const bool mfma = a->dtype == SATTN_BF16;
+  // Few queries with long lists (the decode shape): one workgroup per (query, slice) gathers each
+  // listed row once for all heads.
+  const bool by_slice = mfma && sattn::indexed_slice_supported(p) && rows * parts < 4096;
   if (parts == 1) {
     p.part_len = a->topk > 0 ? a->topk : 1;
+    if (by_slice) return launch_status(sattn::launch_indexed_slice(p, stream));
     if (mfma && sattn::indexed_mfma_supported(p)) return launch_status(sattn::launch_indexed_mfma(p, stream));
     return launch_status(sattn::launch_indexed_valu(p, elem, stream));
   }
@@ -223,7 +227,8 @@ sattn_status indexed_fwd_with_workspace(const sattn_indexed_args *a, void *works
   p.num_parts = parts;
   p.part_o = reinterpret_cast<float *>(ws);
   p.part_lse = reinterpret_cast<float *>(ws + part_o_bytes(a->num_splits, rows, a->num_heads, a->head_dim));
-  hipError_t e = (mfma && sattn::indexed_mfma_supported(p)) ? sattn::launch_indexed_mfma(p, stream)
+  hipError_t e = by_slice ? sattn::launch_indexed_slice(p, stream)
+                 : (mfma && sattn::indexed_mfma_supported(p)) ? sattn::launch_indexed_mfma(p, stream)
                                                              : sattn::launch_indexed_valu(p, elem, stream);
   if (e != hipSuccess) return SATTN_ERR_LAUNCH;
   sattn::MergeParams m;

@@ -94,6 +94,10 @@ bool window_mfma_supported(const WindowParams &p);
 hipError_t launch_window_mfma(const WindowParams &p, hipStream_t stream);
 bool indexed_mfma_supported(const IndexedParams &p);
 hipError_t launch_indexed_mfma(const IndexedParams &p, hipStream_t stream);
+// One workgroup per (query, list slice) for all heads of the query (few queries, long lists); split
+// launches write partials for launch_merge.
+bool indexed_slice_supported(const IndexedParams &p);
+hipError_t launch_indexed_slice(const IndexedParams &p, hipStream_t stream);
 bool indexed_fp8_supported(const IndexedParams &p);
 hipError_t launch_indexed_fp8(const IndexedParams &p, hipStream_t stream);
 

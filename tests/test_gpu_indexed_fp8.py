@@ -77,18 +77,20 @@ def test_indexed_fp8_matches_oracle(dev, case):
 
 @pytest.mark.parametrize("rd,mode,splits", [(64, 0, 1), (0, 1, 1), (64, 2, 4), (0, 0, 2)])
 def test_indexed_fp8_equals_bf16_kernel_on_dequantised_rows(dev, rd, mode, splits):
-    """Rows scaled over 2^-4..2^4 (every scale exponent path).  The bf16 kernel places list entry
+    """Rows scaled over 2^-4..2^4 (every scale exponent path).  The bf16 kernel of launches with 4096
+    or more (query, slice) pairs (one wave per query, 32 heads and slice) places list entry
     (r % 4) * 8 + r / 4 of a 32-entry block in tile row r, the fp8 kernel entry r; the bf16 kernel is
     given each block's entries in that order so that both see the same tiles and sum in the same
     order.  Lists of 384 entries (12 blocks) with pads; slices are whole blocks."""
-    q, kv8, sc, rope, idx, sinks = _case(11 + rd + mode, 2, 9, 32, 800, 384, rd, 5, spread=4)
+    M = 2048  # 4096 queries: the bf16 launch that sums a slice's blocks in order within one wave
+    q, kv8, sc, rope, idx, sinks = _case(11 + rd + mode, 2, M, 32, 800, 384, rd, 5, spread=4)
     rows = torch.from_numpy(F8.dequant_rows(kv8, sc, rope)).to(torch.bfloat16)
     assert torch.equal(rows.float(), torch.from_numpy(F8.dequant_rows(kv8, sc, rope)))  # exact in bf16
     r = torch.arange(32)
     entry_of_row = (r % 4) * 8 + r // 4
-    idx16 = idx.clone().view(2, 9, 12, 32)
-    idx16[..., entry_of_row] = idx.view(2, 9, 12, 32)
-    idx16 = idx16.view(2, 9, 384).contiguous()
+    idx16 = idx.clone().view(2, M, 12, 32)
+    idx16[..., entry_of_row] = idx.view(2, M, 12, 32)
+    idx16 = idx16.view(2, M, 384).contiguous()
     o8, l8 = _run(dev, q, kv8, sc, rope, idx, sinks, mode, splits)
     o16, l16 = sattn.indexed_fwd(q.to(dev), rows.to(dev), idx16.to(dev), sinks=sinks.to(dev) if mode else None,
                                  sink_mode=SINK_NAMES[mode], num_splits=splits, return_lse=True)
