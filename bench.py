@@ -52,16 +52,18 @@ def _src_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def _traffic(workload: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they match the current kernels."""
-    path = os.path.join(PROFILES, f"traffic_{workload}.json")
+def _counters(workload: str):
+    """rocprofv3 counter summary of a workload (profiles/counters_<workload>.json), if it was taken of
+    the current kernel sources: HBM bytes per launch (FETCH_SIZE and WRITE_SIZE scaled by a plain
+    device copy's readings) and the dominant kernel's MfmaUtil, VALUBusy and LdsUtil."""
+    path = os.path.join(PROFILES, f"counters_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
     if rec.get("kernel_source_sha") != _src_hash():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec
 
 
 class Workload:
@@ -281,7 +283,6 @@ class IndexerWorkload(Workload):
         import workloads as W
         super().__init__(device)
         self.name = name
-        self.bound = "hbm"
         self.case0 = None
         self.sets = []
         for s in range(n_sets):
@@ -296,6 +297,10 @@ class IndexerWorkload(Workload):
         self.pairs = sum(vis)  # (query, visible compressed row) pairs scored
         self.bytes = q_len * rank * 2 + n_comp * rank * 2 + 4 + q_len * K * 4
         self.flops = 2 * rank * self.pairs
+        # Bound: every workgroup (32 queries) must bring the index keys of the rows visible to its last
+        # query from L2 into its CU at least once (one score pass); the kernel makes two such passes.
+        self.bound = "l2"
+        self.l2_bytes = sum(vis[min(q_len, t + 32) - 1] for t in range(0, q_len, 32)) * rank * 2
         self.unit = "scored pairs/s"
         self.config = dict(workload=name, batch=1, q_len=q_len, n_comp=n_comp, rank=rank, window=window,
                            ratio=ratio, topk=topk, start_pos=start_pos, input_sets=n_sets)
@@ -387,16 +392,35 @@ def time_workload(wl, steps, warmup):
     return wall, mean_ev, ev_ms[len(ev_ms) // 2], replays * group
 
 
+L2_PEAK_GBS = 256 * 64 * 2.4  # L2 -> CU: 256 CUs x 64 bytes per clock x 2.4 GHz (39.3 TB/s)
+
+
 def roofline(wl, kernel_ms):
+    """Algorithmic rate of one launch against its bound's peak, beside the counter-based rates of the
+    same launch (HBM bytes per launch / time / HBM peak, and the dominant kernel's MFMA, VALU and LDS
+    utilisation) when a counter summary of the current kernels is committed under profiles/."""
     sec = kernel_ms / 1e3
+    ctr = _counters(wl.name)
+    traffic = ctr.get("hbm_bytes_per_launch") if ctr else None
+    counter = None
+    if ctr:
+        counter = {"hbm_gbs": round(traffic / sec / 1e9, 1), "hbm_frac": round(traffic / sec / 1e9 / HBM_PEAK_GBS, 4),
+                   "kernel": ctr.get("dominant_kernel"), "mfma_util_pct": ctr.get("mfma_util_pct"),
+                   "valu_busy_pct": ctr.get("valu_busy_pct"), "lds_util_pct": ctr.get("lds_util_pct")}
     if wl.bound == "mfma":
         ach = wl.flops / sec / 1e12
         return {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": _traffic(wl.name),
+                "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": traffic, "counter": counter,
                 "algorithmic_flops_per_launch": wl.flops}
+    if wl.bound == "l2":
+        ach = wl.l2_bytes / sec / 1e9
+        return {"bound": "l2", "achieved": round(ach, 1), "peak": round(L2_PEAK_GBS, 1), "unit": "GB/s",
+                "frac": round(ach / L2_PEAK_GBS, 4), "traffic": traffic, "counter": counter,
+                "algorithmic_l2_bytes_per_launch": wl.l2_bytes, "algorithmic_bytes_per_launch": wl.bytes,
+                "hbm_frac": round(wl.bytes / sec / 1e9 / HBM_PEAK_GBS, 4)}
     ach = wl.bytes / sec / 1e9
     return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": _traffic(wl.name),
+            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic, "counter": counter,
             "algorithmic_bytes_per_launch": wl.bytes,
             "mfma_tflops": round(wl.flops / sec / 1e12, 2)}
 

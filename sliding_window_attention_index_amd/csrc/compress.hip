@@ -171,6 +171,10 @@ __global__ __launch_bounds__(256) void compress_pool_kernel(CompressParams p) {
 
 template <typename T>
 hipError_t launch_t(const CompressParams &p, dim3 grid, hipStream_t stream) {
+  if (trace_on())
+    trace("compress_pool_kernel<%s, ratio=%d> grid=%u block=256 rows=%lld head_dim=%d overlap=%d",
+          sizeof(T) == 2 ? "bf16" : "fp32", p.ratio, grid.x, static_cast<long long>(p.batch) * (p.seq_len / p.ratio),
+          p.head_dim, p.overlap);
   switch (p.ratio) {
     case 1: hipLaunchKernelGGL((compress_pool_kernel<T, 1>), grid, dim3(256), 0, stream, p); break;
     case 2: hipLaunchKernelGGL((compress_pool_kernel<T, 2>), grid, dim3(256), 0, stream, p); break;

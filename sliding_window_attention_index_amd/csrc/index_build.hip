@@ -111,10 +111,16 @@ hipError_t launch_build_topk_idxs(const BuildIdxParams &a, hipStream_t stream) {
   if (vec && K >= 256) {
     const int64_t items = static_cast<int64_t>(a.batch) * a.q_len * ((K / 4 + kPiece - 1) / kPiece);
     const int64_t wgs = std::min<int64_t>((items + 3) / 4, static_cast<int64_t>(cus) * 1024);  // ~one piece per wave
+    if (trace_on())
+      trace("build_topk_idxs_rows grid=%lld block=256 pieces=%lld lists=%lld entries=%d", static_cast<long long>(wgs),
+            static_cast<long long>(items), static_cast<long long>(a.batch) * a.q_len, K);
     hipLaunchKernelGGL(build_topk_idxs_rows, dim3(static_cast<unsigned>(wgs)), dim3(256), 0, stream, a);
     return hipGetLastError();
   }
   const int64_t blocks = std::min<int64_t>((total + 255) / 256, static_cast<int64_t>(cus) * 16);
+  if (trace_on())
+    trace("build_topk_idxs_kernel<vec=%d> grid=%lld block=256 lists=%lld entries=%d", vec ? 1 : 0,
+          static_cast<long long>(blocks), static_cast<long long>(a.batch) * a.q_len, K);
   if (vec)
     hipLaunchKernelGGL(build_topk_idxs_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, a);
   else

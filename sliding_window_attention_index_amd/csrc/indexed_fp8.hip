@@ -364,6 +364,11 @@ hipError_t launch(const IndexedParams &p, hipStream_t stream) {
   const int64_t tasks = static_cast<int64_t>(p.batch) * p.q_len * n_hg * p.num_parts;
   const int64_t blocks = (tasks + 3) / 4;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (trace_on())
+    trace("indexed_fp8_mfma<rope_dims=%d, NT=%d> grid=%lld block=256 (rows=%lld x head groups=%d x slices=%d of %d "
+          "entries) kv_len=%d topk=%d sink_mode=%d", RD, NT, static_cast<long long>(blocks),
+          static_cast<long long>(p.batch) * p.q_len, p.num_heads / 32, p.num_parts, p.part_len, p.kv_len, p.topk,
+          p.sink_mode);
   hipLaunchKernelGGL((indexed_fp8_mfma<RD, NT>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }

@@ -345,6 +345,11 @@ hipError_t launch(const IndexedParams &p, hipStream_t stream) {
   const int64_t tasks = static_cast<int64_t>(p.batch) * p.q_len * n_hg * p.num_parts;
   const int64_t blocks = (tasks + 3) / 4;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (trace_on())
+    trace("indexed_fwd_mfma<D=%d, NT=%d, mass=%d> grid=%lld block=256 tasks=%lld (rows=%lld x head groups=%d x "
+          "slices=%d of %d entries) kv_len=%d topk=%d sink_mode=%d", D, NT, kMass ? 1 : 0, static_cast<long long>(blocks),
+          static_cast<long long>(tasks), static_cast<long long>(p.batch) * p.q_len, n_hg, p.num_parts, p.part_len,
+          p.kv_len, p.topk, p.sink_mode);
   hipLaunchKernelGGL((indexed_fwd_mfma<D, NT, kMass>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }

@@ -357,6 +357,10 @@ template <int D, int NHG>
 hipError_t launch(const IndexedParams &p, hipStream_t stream) {
   const int64_t blocks = static_cast<int64_t>(p.batch) * p.q_len * p.num_parts;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (trace_on())
+    trace("indexed_slice_mfma<D=%d, head groups=%d> grid=%lld block=256 (rows=%lld x slices=%d of %d entries) "
+          "kv_len=%d topk=%d sink_mode=%d", D, NHG, static_cast<long long>(blocks),
+          static_cast<long long>(p.batch) * p.q_len, p.num_parts, p.part_len, p.kv_len, p.topk, p.sink_mode);
   hipLaunchKernelGGL((indexed_slice_mfma<D, NHG>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }

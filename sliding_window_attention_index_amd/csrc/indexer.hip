@@ -608,6 +608,9 @@ template <int S>
 hipError_t launch_rank(const IndexerParams &p, hipStream_t stream) {
   constexpr int NW = S <= 4 ? 16 : 8;  // 128 VGPRs a lane at 16 waves; rank 128 needs more
   const dim3 grid(static_cast<unsigned>((p.q_len + 31) / 32), static_cast<unsigned>(p.batch));
+  if (trace_on())
+    trace("indexer_topk_kernel<rank=%d, waves=%d> grid=%ux%u block=%d n_comp=%d topk=%d window=%d ratio=%d", 16 * S, NW,
+          grid.x, grid.y, 64 * NW, p.n_comp, p.topk, p.window, p.ratio);
   hipLaunchKernelGGL((indexer_topk_kernel<S, NW>), grid, dim3(64 * NW), 0, stream, p);
   return hipGetLastError();
 }

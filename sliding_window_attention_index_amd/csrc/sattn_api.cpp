@@ -10,7 +10,11 @@
 #include <cstdint>
 
 #include <math.h>
+#include <stdarg.h>
 #include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "sattn_kernels.hpp"
 
@@ -43,6 +47,27 @@ size_t part_lse_bytes(int64_t parts, int64_t rows, int64_t heads) {
 }
 
 }  // namespace
+
+namespace sattn {
+
+bool trace_on() {
+  static const bool on = [] {
+    const char *e = getenv("SATTN_TRACE");
+    return e != nullptr && e[0] != '\0' && strcmp(e, "0") != 0;
+  }();
+  return on;
+}
+
+void trace(const char *fmt, ...) {
+  char line[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(line, sizeof line, fmt, ap);
+  va_end(ap);
+  fprintf(stderr, "[sattn] %s\n", line);
+}
+
+}  // namespace sattn
 
 extern "C" {
 

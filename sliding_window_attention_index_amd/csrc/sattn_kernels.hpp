@@ -84,6 +84,12 @@ struct MergeParams {
   float *lse;
 };
 
+// Host-side launch trace: with SATTN_TRACE=1 in the environment (read once), every launcher prints
+// one line per kernel launch to stderr (kernel variant, grid, and the sizes that chose them) before
+// launching.  Off by default; nothing else changes.
+bool trace_on();
+void trace(const char *fmt, ...) __attribute__((format(printf, 1, 2)));
+
 // Launchers return hipSuccess or the launch error; they never synchronise.
 hipError_t launch_window_valu(const WindowParams &p, int elem_type, hipStream_t stream);
 hipError_t launch_indexed_valu(const IndexedParams &p, int elem_type, hipStream_t stream);

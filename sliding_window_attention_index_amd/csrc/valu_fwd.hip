@@ -340,6 +340,10 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
 
 hipError_t launch_window_valu(const WindowParams &p, int elem_type, hipStream_t stream) {
   const dim3 grid((p.max_seqlen + kWavesPerBlock - 1) / kWavesPerBlock, p.num_seqs, p.num_heads);
+  if (trace_on())
+    trace("window_fwd_valu<%s> grid=%ux%ux%u block=%d head_dim=%d group=%d window=(%d, %d) sink_mode=%d",
+          elem_type == kF32 ? "fp32" : "bf16", grid.x, grid.y, grid.z, 64 * kWavesPerBlock, p.head_dim, p.group,
+          p.window_left, p.window_right, p.sink_mode);
   if (elem_type == kF32)
     hipLaunchKernelGGL(window_fwd_valu<float>, grid, dim3(64 * kWavesPerBlock), 0, stream, p);
   else
@@ -350,6 +354,10 @@ hipError_t launch_window_valu(const WindowParams &p, int elem_type, hipStream_t 
 hipError_t launch_indexed_valu(const IndexedParams &p, int elem_type, hipStream_t stream) {
   const int64_t BM = static_cast<int64_t>(p.batch) * p.q_len;
   const dim3 grid(static_cast<unsigned>((BM + kWavesPerBlock - 1) / kWavesPerBlock), p.num_heads, p.num_parts);
+  if (trace_on())
+    trace("indexed_fwd_valu<%s> grid=%ux%ux%u block=%d head_dim=%d slices=%d of %d entries topk=%d sink_mode=%d",
+          elem_type == kF32 ? "fp32" : "bf16", grid.x, grid.y, grid.z, 64 * kWavesPerBlock, p.head_dim, p.num_parts,
+          p.part_len, p.topk, p.sink_mode);
   if (elem_type == kF32)
     hipLaunchKernelGGL(indexed_fwd_valu<float>, grid, dim3(64 * kWavesPerBlock), 0, stream, p);
   else
@@ -360,6 +368,9 @@ hipError_t launch_indexed_valu(const IndexedParams &p, int elem_type, hipStream_
 hipError_t launch_block_mass_valu(const IndexedParams &p, int elem_type, hipStream_t stream) {
   const int64_t BM = static_cast<int64_t>(p.batch) * p.q_len;
   const dim3 grid(static_cast<unsigned>((BM + kWavesPerBlock - 1) / kWavesPerBlock), p.num_heads);
+  if (trace_on())
+    trace("block_mass_valu<%s> grid=%ux%u block=%d head_dim=%d block_keys=%d bins=%d", elem_type == kF32 ? "fp32" : "bf16",
+          grid.x, grid.y, 64 * kWavesPerBlock, p.head_dim, p.block_keys, p.n_bins);
   if (elem_type == kF32)
     hipLaunchKernelGGL(block_mass_valu<float>, grid, dim3(64 * kWavesPerBlock), 0, stream, p);
   else
@@ -375,6 +386,10 @@ hipError_t launch_merge(const MergeParams &p, hipStream_t stream) {
     const int64_t blocks = (threads + 255) / 256;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     const dim3 grid(static_cast<unsigned>(blocks));
+    if (trace_on())
+      trace("merge4_kernel<%s> grid=%lld block=256 parts=%d rows=%d heads=%d head_dim=%d sink_mode=%d",
+            p.out_type == kF32 ? "fp32" : "bf16", static_cast<long long>(blocks), p.num_parts, p.rows, p.num_heads,
+            p.head_dim, p.sink_mode);
     if (p.out_type == kF32)
       hipLaunchKernelGGL(merge4_kernel<float>, grid, dim3(256), 0, stream, p);
     else
@@ -382,6 +397,9 @@ hipError_t launch_merge(const MergeParams &p, hipStream_t stream) {
     return hipGetLastError();
   }
   const dim3 grid(static_cast<unsigned>((RH + 3) / 4));
+  if (trace_on())
+    trace("merge_kernel<%s> grid=%u block=256 parts=%d rows=%d heads=%d head_dim=%d sink_mode=%d",
+          p.out_type == kF32 ? "fp32" : "bf16", grid.x, p.num_parts, p.rows, p.num_heads, p.head_dim, p.sink_mode);
   if (p.out_type == kF32)
     hipLaunchKernelGGL(merge_kernel<float>, grid, dim3(256), 0, stream, p);
   else

@@ -327,6 +327,11 @@ hipError_t launch(const WindowParams &p, hipStream_t stream) {
   if (n_tiles <= 0) return hipSuccess;
   const int64_t per_xcd = (n_tiles + kXcds - 1) / kXcds;
   if (per_xcd * kXcds > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (trace_on())
+    trace("window_fwd_mfma<D=%d, G=%d> grid=%lld block=256 tiles=%lld (%lld per sequence, %d queries each) seqs=%d "
+          "kv_heads=%d window=(%d, %d) sink_mode=%d", D, G, static_cast<long long>(per_xcd * kXcds),
+          static_cast<long long>(n_tiles), static_cast<long long>(tiles_per_seq), QT, p.num_seqs, p.num_kv_heads,
+          p.window_left, p.window_right, p.sink_mode);
   hipLaunchKernelGGL((window_fwd_mfma<D, G>), dim3(static_cast<unsigned>(per_xcd * kXcds)), dim3(256), 0, stream, p,
                      static_cast<int>(tiles_per_seq), static_cast<int>(n_tiles));
   return hipGetLastError();
