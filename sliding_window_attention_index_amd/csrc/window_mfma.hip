@@ -132,9 +132,18 @@ __global__ __launch_bounds__(256, D == 128 && (G <= 4 || G == 32) ? 3 : 1) void 
     }
   };
 
-  // This lane's sink, read without a branch (no sinks: an empty buffer, which reads as 0).
-  const __amdgpu_buffer_rsrc_t srs = make_rsrc(p.sinks, p.sink_mode != kSinkNone ? static_cast<uint32_t>(H) * 4 : 0u);
-  const float sink = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(srs, static_cast<uint32_t>(head) * 4, 0, 0));
+  // This lane's sink: the G sinks of the KV head's query heads come through scalar loads (one address
+  // for the whole wave) and each lane picks its own.  A vector load here would be waited for before
+  // the Q rows and the first K/V blocks are requested, a memory round trip more per tile.
+  float sink = 0.0f;
+  if (p.sink_mode != kSinkNone) {
+    const float *sg = p.sinks + g * G;
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const float sv = sg[i];
+      sink = n % G == i ? sv : sink;
+    }
+  }
 
   // ---- Q operand in registers: row n, logical chunks h S .. h S + S - 1 (rows past Lq read 0) ----
   bf16x8 qf[S];
