@@ -9,13 +9,19 @@
 //
 // gfx950 mapping: one wave64 per task (a query, 32 of its heads, one slice of its list), four
 // independent waves per workgroup, as in the bf16 kernel.  Per 32-row block the wave DMAs into one
-// of NT wave-private LDS slots: the rows' fp8 bytes (row-major), their scales and, when RD = 64,
-// their bf16 rotary dims straight into a swizzled 32 x 64 tile.  When the block's DMAs have landed
-// the wave converts its fp8 bytes to bf16 with v_cvt_scalef32_pk_bf16_fp8 (an fp8 value times a
-// power of two is exact in bf16) into swizzled 32 x 64 tiles, so that the product code of the
-// bf16 kernel runs unchanged on two 64-dim tiles: with the MFMA step mapping of logical chunk
-// h*S + s, lanes of half 0 read only dims 0..63 and lanes of half 1 only dims 64..127.  The fp8
-// rows halve (RD = 0) or cut by a quarter (RD = 64) the bytes gathered per row.
+// of NT wave-private LDS slots: the rows' fp8 bytes (16-byte chunks swizzled per row), their
+// scales and, when RD = 64, their bf16 rotary dims straight into a swizzled 32 x 64 tile.  The
+// codes never go back to LDS as bf16: each operand is converted in registers
+// (v_cvt_scalef32_pk_bf16_fp8) right before its MFMA.
+//   * K (A operand of S^T = K . Q^T): lane (row n, half h) reads its row's codes and converts
+//     them times the row's scale, so the logits are those of the dequantised rows.
+//   * V^T (A operand of O^T = V^T . P^T): ds_read_b64_tr_b8 hands each lane 8 codes of one dim
+//     from 8 rows; they are converted unscaled and each key's scale moves to its probability
+//     instead (sum_j p_j (2^e_j c_jd) = sum_j (p_j 2^e_j) c_jd).
+// A power of two times a bf16 or an e4m3 value is exact in bf16 (away from the subnormal range),
+// so every product entering an MFMA equals the bf16 kernel's on the dequantised rows, in the
+// same MFMA step mapping: the two kernels agree bit for bit.  The fp8 rows halve (RD = 0) or cut
+// by a quarter (RD = 64) the bytes gathered per row.
 #include "lds_tile.hpp"
 #include "sattn_device.hpp"
 #include "sattn_kernels.hpp"
@@ -67,30 +73,78 @@ __device__ __forceinline__ u32x4 fp8x8_to_bf16(uint32_t w0, uint32_t w1, float s
   return r;
 }
 
+template <int OFF>
+__device__ __forceinline__ u32x2 ds_read_b64(uint32_t addr) {
+  u32x2 r;
+  asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+
+// Eight LDS bytes per lane, transposed across lanes: in each group of 16 lanes, lane i receives as
+// its byte e (e = 0..7) byte i % 8 of the 8 bytes that lane 2e + i / 8 of the group addresses.
+template <int OFF>
+__device__ __forceinline__ u32x2 ds_read_tr_b8(uint32_t addr) {
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+
+// The block's probabilities as softmax_probs makes them (same exponentials, same sum into l):
+// pb = bf16(p) for the bf16 rotary dims (when kPlain), pbs = bf16(p * scale of the key) for the
+// fp8 dims.  Accumulator element r of lane (n, h) is key 8 (r / 4) + 4h + r % 4, whose scale is
+// ks[r / 4][r % 4].
+template <bool kPlain>
+__device__ __forceinline__ void softmax_probs_scaled(const f32x16 &st, RowSoftmax &rs, float c, const u32x4 (&ks)[4],
+                                                     bf16x8 (&pb)[2], bf16x8 (&pbs)[2]) {
+  const float mc = rs.m == kNegInf ? 0.0f : rs.m * c;
+  float l0 = 0.0f, l1 = 0.0f;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      const int r = 8 * t + j;
+      const float e0 = fast_exp2(fmaf(st[r], c, -mc));
+      const float e1 = fast_exp2(fmaf(st[r + 1], c, -mc));
+      l0 += e0;
+      l1 += e1;
+      if constexpr (kPlain) {
+        pb[t][j] = static_cast<__bf16>(e0);
+        pb[t][j + 1] = static_cast<__bf16>(e1);
+      }
+      pbs[t][j] = static_cast<__bf16>(e0 * __uint_as_float(ks[r >> 2][r & 3]));
+      pbs[t][j + 1] = static_cast<__bf16>(e1 * __uint_as_float(ks[r >> 2][(r & 3) + 1]));
+    }
+  }
+  rs.l += l0 + l1;
+}
+
 template <int RD, int NT>
 __global__ __launch_bounds__(256) void indexed_fp8_mfma(IndexedParams p) {
   constexpr int D = 128;
   constexpr int S = D / 16;   // MFMA steps over head_dim
   constexpr int DB = D / 32;  // 32-wide blocks of output dims
   using T64 = SwizzledTile<64>;
-  constexpr int D8 = D - RD;                          // fp8 bytes per row
-  constexpr int kF8Bytes = kBlockKeys * D8;           // a block's fp8 bytes
-  constexpr int kRopeBytes = RD ? T64::kBytes : 0;    // a block's rotary tile
-  constexpr int kSlotBytes = kRopeBytes + kF8Bytes + 256;  // + scales (64 lanes x 4 bytes)
+  constexpr int D8 = D - RD;                        // fp8 bytes per row
+  constexpr int DB8 = D8 / 32;                      // output dim blocks read from fp8 codes
+  constexpr int kChunks8 = D8 / 16;                 // 16-byte chunks of an fp8 row
+  constexpr int kRowsPer256 = 256 / D8;             // fp8 rows per 256 bytes of LDS
+  constexpr int kF8Bytes = kBlockKeys * D8;         // a block's fp8 bytes
+  constexpr int kRopeBytes = RD ? T64::kBytes : 0;  // a block's rotary tile
+  constexpr int kScaleOff = kRopeBytes + kF8Bytes;  // a block's scales (64 lanes x 4 bytes)
+  constexpr int kSlotBytes = kScaleOff + 256;
   constexpr int kF8Dma = kF8Bytes / 1024;
   constexpr int kRopeDma = RD ? T64::kDmaPerTile : 0;
-  constexpr int kDpb = kF8Dma + kRopeDma + 1;         // DMA instructions per block
-  constexpr int kConvTiles = RD ? 1 : 2;              // 64-dim tiles converted from fp8
+  constexpr int kDpb = kF8Dma + kRopeDma + 1;       // DMA instructions per block
   static_assert(RD == 0 || RD == 64, "rotary dims");
   static_assert((NT & (NT - 1)) == 0 && NT >= 2 && NT <= 4, "ring size");
   static_assert(kSlotBytes % 256 == 0, "slot bases keep bits 4..7 clear");
+  static_assert(kSlotBytes >= 32 * 128, "the epilogue stages 32 rows of 128 bytes in a slot");
   __shared__ __attribute__((aligned(1024))) char ring[4][NT * kSlotBytes];
-  __shared__ __attribute__((aligned(1024))) char conv[4][kConvTiles * T64::kBytes];
   __shared__ __attribute__((aligned(16))) int32_t lists[4][kIdxCap];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = lane_id();
-  const int h = lane >> 5;   // half of the wave: which half of head_dim / which key quads
+  const int h = lane >> 5;   // half of the wave: which 8 dims of each MFMA step / which key quads
   const int n = lane & 31;   // key row (A operand) / head (B operand and outputs)
   const int H = p.num_heads, N = p.kv_len, K = p.topk;
   const int n_hg = H / 32;
@@ -107,12 +161,13 @@ __global__ __launch_bounds__(256) void indexed_fp8_mfma(IndexedParams p) {
   const bool key0 = p.sink_mode == kSinkKey0;
   const bool null_sink = !partial && p.sink_mode == kSinkNull;
 
-  // B operand of S^T: q[bt, head0 + n, h*D/2 + 8s .. +8] (logical chunk h*S + s of the row).
+  // B operand of S^T: q[bt, head0 + n, 16s + 8h .. +8], the bf16 kernel's MFMA steps: steps
+  // 0 .. D8 / 16 - 1 cover the fp8 dims, the rest the rotary dims.
   bf16x8 qf[S];
   {
-    const __bf16 *qrow = static_cast<const __bf16 *>(p.q) + (bt * H + head0 + n) * D + h * (D / 2);
+    const __bf16 *qrow = static_cast<const __bf16 *>(p.q) + (bt * H + head0 + n) * D + 8 * h;
 #pragma unroll
-    for (int s = 0; s < S; ++s) qf[s] = *reinterpret_cast<const bf16x8 *>(qrow + s * 8);
+    for (int s = 0; s < S; ++s) qf[s] = *reinterpret_cast<const bf16x8 *>(qrow + s * 16);
   }
   const float c = p.scale_log2;  // > 0 on this path
   const float sink_raw = p.sinks ? p.sinks[head0 + n] * kLog2e / c : 0.0f;  // raw logit units
@@ -136,16 +191,15 @@ __global__ __launch_bounds__(256) void indexed_fp8_mfma(IndexedParams p) {
   const __amdgpu_buffer_rsrc_t lrs = make_rsrc(p.idx + bt * K, static_cast<uint32_t>(K) * 4u);
   char *const wring = ring[wave];
   const uint32_t ring_addr = lds_addr(wring);
-  const uint32_t conv_addr = lds_addr(conv[wave]);
   int32_t *list = lists[wave];
   const uint32_t list_addr = lds_addr(list);
 
-  // Slot layout: [rotary tile (RD = 64)][fp8 bytes, row-major][scales].  Tile row r holds list
-  // entry r of the block.  DMA instruction u of the fp8 bytes covers rows 1024 u / D8 ..; lane l
-  // fetches 16 bytes of row (1024 u + 16 l) / D8.
-  // The entries a lane needs for one block: the rows of its fp8 pieces, of its rotary pieces and
-  // (lanes 0..31) of its scale, read together and waited for once.
-  constexpr int kF8LanesPerRow = D8 / 16;
+  // Slot layout: [rotary tile (RD = 64)][fp8 rows][scales].  Row r of a block (list entry r) keeps
+  // its fp8 16-byte chunk q at chunk q ^ ((r / kRowsPer256) % kChunks8) of its D8 bytes: 16
+  // consecutive rows reading one logical chunk, and the 8 rows x 2 chunks of a transposed read,
+  // then fall in distinct banks.  DMA instruction u of the fp8 bytes fills LDS bytes 1024 u ..;
+  // lane l fetches the chunk that belongs at byte 1024 u + 16 l.
+  auto f8_swz = [](int r) { return (r / kRowsPer256) & (kChunks8 - 1); };
   constexpr int kReads = kF8Dma + kRopeDma + 1;
   auto issue_block = [&](int j) {
     char *slot = wring + (j & (NT - 1)) * kSlotBytes;
@@ -162,8 +216,12 @@ __global__ __launch_bounds__(256) void indexed_fp8_mfma(IndexedParams p) {
     xs[kReads - 1] = ds_read_b32_raw(lbase + (lane & (kBlockKeys - 1)) * 4);
     lgkm_fence<0>(xs);
 #pragma unroll
-    for (int u = 0; u < kF8Dma; ++u)
-      dma16(f8rs, slot + kRopeBytes + u * 1024, xs[u] * D8 + (lane % kF8LanesPerRow) * 16);
+    for (int u = 0; u < kF8Dma; ++u) {
+      const int pos = 1024 * u + 16 * lane;
+      const int row = pos / D8;
+      const int chunk = ((pos % D8) / 16) ^ f8_swz(row);
+      dma16(f8rs, slot + kRopeBytes + u * 1024, xs[u] * D8 + chunk * 16);
+    }
 #pragma unroll
     for (int u = 0; u < kRopeDma; ++u) {
       int row, chunk;
@@ -173,44 +231,26 @@ __global__ __launch_bounds__(256) void indexed_fp8_mfma(IndexedParams p) {
     }
     {
       const uint32_t x = xs[kReads - 1];
-      dma4(scrs, slot + kRopeBytes + kF8Bytes, lane < kBlockKeys ? x * 4u : 0xfffff000u);
+      dma4(scrs, slot + kScaleOff, lane < kBlockKeys ? x * 4u : 0xfffff000u);
     }
   };
 
-  // fp8 -> bf16: lane (r = lane / 2, g = lane % 2) converts half g of row r's fp8 bytes into the
-  // 64-dim tile(s): RD = 0, 64 bytes into tile g (dims 64 g ..); RD = 64, 32 bytes into chunks
-  // 4 g .. 4 g + 3 of the one converted tile.
-  const int cr = lane >> 1, cg = lane & 1;
-  constexpr int kConvBytesPerLane = D8 / 2;
-  auto convert_block = [&](int slot_i) {
-    const uint32_t sa = ring_addr + slot_i * kSlotBytes;
-    const uint32_t src = sa + kRopeBytes + cr * D8 + cg * kConvBytesPerLane;
-    u32x4 raw[kConvBytesPerLane / 16];
-#pragma unroll
-    for (int i = 0; i < kConvBytesPerLane / 16; ++i) raw[i] = ds_read_b128<0>(src + 16 * i);
-    int sc_bits[1];
-    sc_bits[0] = ds_read_i32(sa + kRopeBytes + kF8Bytes + cr * 4);
-    lgkm_fence<0>(raw);
-    const float scale = __int_as_float(sc_bits[0]);
-    const uint32_t tile = conv_addr + (RD ? 0 : cg * T64::kBytes);
-    const int chunk0 = RD ? 4 * cg : 0;
-#pragma unroll
-    for (int i = 0; i < kConvBytesPerLane / 16; ++i) {
-      const u32x4 lo = fp8x8_to_bf16(raw[i][0], raw[i][1], scale);
-      const u32x4 hi = fp8x8_to_bf16(raw[i][2], raw[i][3], scale);
-      ds_write_b128<0>(tile + T64::offset(cr, chunk0 + 2 * i), lo);
-      ds_write_b128<0>(tile + T64::offset(cr, chunk0 + 2 * i + 1), hi);
-    }
-  };
-
-  // LDS operand addresses (tile bases have bits 4..7 clear).  K rows: lane (n, h) reads logical
-  // chunk s of row n of its half's tile at kbase ^ 16 s; V^T quads of dims 32 db .. at the D = 64
-  // tile addresses of the bf16 kernel, in the tile of dims 64 (db / 2) ...
-  const uint32_t tileA = conv_addr;
-  auto tileB = [&](int slot_i) -> uint32_t {
-    return RD ? ring_addr + slot_i * kSlotBytes : conv_addr + T64::kBytes;
-  };
-  const uint32_t koff = T64::offset(n, 0);
+  // Per-lane LDS offsets inside a slot (the XORed terms stay inside one row).
+  //  K, fp8 step s: bytes 16 s + 8 h .. + 7 of row n at (k8 ^ 16 s).  K, rotary step s (RD = 64):
+  //  logical chunk 2 (s - D8 / 16) + h of row n of the tile at (kr ^ 32 (s - D8 / 16)).
+  const uint32_t k8 = kRopeBytes + n * D8 + 16 * f8_swz(n) + 8 * h;
+  const uint32_t kr = T64::offset(n, h);
+  //  V^T, fp8 dims 32 db + (lane & 31): lane (group g16, index i16) reads 8 bytes of row
+  //  8 (i16 / 8) + 4h + (i16 / 2) % 4 (+ 16 tt), dims 32 db + 16 (g16 % 2) + 8 (i16 % 2) ..: after
+  //  the transposed read, lane (n, h) holds the codes of dim 32 db + n for keys 4h .. 4h + 3 and
+  //  8 + 4h .. 8 + 4h + 3 (+ 16 tt), the key order of the probabilities' B operand.
+  uint32_t v8;
+  {
+    const int g16 = lane >> 4, i16 = lane & 15;
+    const int row = 8 * (i16 >> 3) + 4 * h + ((i16 >> 1) & 3);
+    v8 = kRopeBytes + row * D8 + 16 * ((g16 & 1) ^ f8_swz(row)) + 8 * (i16 & 1);
+  }
+  //  V^T, rotary dims (RD = 64): the quads of the bf16 kernel's D = 64 tile.
   uint32_t voff;
   {
     const int g16 = lane >> 4, i16 = lane & 15;
@@ -218,30 +258,79 @@ __global__ __launch_bounds__(256) void indexed_fp8_mfma(IndexedParams p) {
     voff = T64::offset(4 * h + (i16 >> 2), c2) + (i16 & 1) * 8;
   }
   constexpr int kRow8 = 8 * T64::kRowBytes;
+  constexpr int kRows16 = 16 * D8;  // 16 fp8 rows (the same swizzle)
 
-  auto compute = [&](int slot_i, uint32_t vmask, uint32_t zmask) {
-    const uint32_t tb = tileB(slot_i);
-    uint32_t kb_ = (h == 0 ? tileA : tb) + koff;
-    asm volatile("" : "+v"(kb_));
-    u32x4 kf[S];
+  // Block j from its slot: row n's list entry is read with the block's operands, and a block
+  // without a row is skipped once it is known.
+  auto compute = [&](int j) {
+    const uint32_t sb = ring_addr + (j & (NT - 1)) * kSlotBytes;
+    // K operand and the scales: this lane's row (K) and its keys' (probabilities).
+    constexpr int kS8 = D8 / 16;  // MFMA steps over fp8 dims
+    u32x2 k8r[kS8];
+    u32x4 krr[S - kS8 > 0 ? S - kS8 : 1];
+    {
+      uint32_t ka = sb + k8;
+      asm volatile("" : "+v"(ka));
 #pragma unroll
-    for (int s = 0; s < S; ++s) kf[s] = ds_read_b128<0>(kb_ ^ (16u * s));
-    lgkm_fence<0>(kf);
+      for (int s = 0; s < kS8; ++s) k8r[s] = ds_read_b64<0>(ka ^ (16u * s));
+    }
+    if constexpr (RD) {
+      uint32_t ka = sb + kr;
+      asm volatile("" : "+v"(ka));
+#pragma unroll
+      for (int s = 0; s < S - kS8; ++s) krr[s] = ds_read_b128<0>(ka ^ (32u * s));
+    }
+    const uint32_t scb = sb + kScaleOff;
+    int ksb[1];
+    ksb[0] = static_cast<int>(ds_read_b32_raw(scb + 4 * n));
+    u32x4 ks[4];
+    {
+      uint32_t pa = scb + 16 * h;
+      asm volatile("" : "+v"(pa));
+      ks[0] = ds_read_b128<0>(pa);
+      ks[1] = ds_read_b128<32>(pa);
+      ks[2] = ds_read_b128<64>(pa);
+      ks[3] = ds_read_b128<96>(pa);
+    }
+    uint32_t xr[1];
+    xr[0] = ds_read_b32_raw(list_addr + (j * kBlockKeys + n) * 4);
+    lgkm_fence<0>(k8r);
+    if constexpr (RD) lgkm_fence<0>(krr);
+    lgkm_fence<0>(ksb);
+    lgkm_fence<0>(ks);
+    lgkm_fence<0>(xr);
+    const uint32_t vmask = static_cast<uint32_t>(__ballot(xr[0] != kBadRow));  // tile row n's entry is a row
+    if (vmask == 0u) return;
+    const uint32_t zmask = key0 ? static_cast<uint32_t>(__ballot(xr[0] == 0u)) : 0u;  // ... and it is row 0
+    const float kscale = __int_as_float(ksb[0]);
     f32x16 st = f32x16{};
 #pragma unroll
-    for (int s = 0; s < S; ++s)
-      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[s]), qf[s], st, 0, 0, 0);
-    uint32_t vbA = tileA + voff, vbB = tb + voff;
-    asm volatile("" : "+v"(vbA), "+v"(vbB));
-    u32x2 vr[4 * DB];
+    for (int s = 0; s < S; ++s) {
+      const u32x4 kf = s < kS8 ? fp8x8_to_bf16(k8r[s][0], k8r[s][1], kscale) : krr[s < kS8 ? 0 : s - kS8];
+      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf), qf[s], st, 0, 0, 0);
+    }
+    // V^T operands.
+    uint32_t va = sb + v8;
+    asm volatile("" : "+v"(va));
+    u32x2 v8r[2 * DB8];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const uint32_t vb = db < 2 ? vbA : vbB;
-      const uint32_t dx = 64u * (db & 1);
-      vr[db * 2] = ds_read_tr_b16<0>(vb ^ dx);
-      vr[db * 2 + 1] = ds_read_tr_b16<kRow8>(vb ^ (dx + 16u));
-      vr[2 * DB + db * 2] = ds_read_tr_b16<2 * kRow8>(vb ^ dx);
-      vr[2 * DB + db * 2 + 1] = ds_read_tr_b16<3 * kRow8>(vb ^ (dx + 16u));
+    for (int db = 0; db < DB8; ++db) {
+      v8r[db] = ds_read_tr_b8<0>(va ^ (32u * db));
+      v8r[DB8 + db] = ds_read_tr_b8<kRows16>(va ^ (32u * db));
+    }
+    constexpr int kV16 = RD ? 8 : 1;
+    u32x2 vr[kV16];
+    if constexpr (RD) {
+      uint32_t vb = sb + voff;
+      asm volatile("" : "+v"(vb));
+#pragma unroll
+      for (int d2 = 0; d2 < 2; ++d2) {
+        const uint32_t dx = 64u * d2;
+        vr[d2 * 2] = ds_read_tr_b16<0>(vb ^ dx);
+        vr[d2 * 2 + 1] = ds_read_tr_b16<kRow8>(vb ^ (dx + 16u));
+        vr[4 + d2 * 2] = ds_read_tr_b16<2 * kRow8>(vb ^ dx);
+        vr[4 + d2 * 2 + 1] = ds_read_tr_b16<3 * kRow8>(vb ^ (dx + 16u));
+      }
     }
     // Accumulator element r of lane (n, h) is key 8*(r/4) + 4h + r%4 of head n.
     if (zmask) bias_block(st, zmask, h, sink_raw);
@@ -251,16 +340,24 @@ __global__ __launch_bounds__(256) void indexed_fp8_mfma(IndexedParams p) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) acc[db] *= alpha;
     }
-    bf16x8 pb[2];
-    softmax_probs(st, rs, c, pb);
-    lgkm_fence<0>(vr);
+    bf16x8 pb[2], pbs[2];
+    softmax_probs_scaled<RD != 0>(st, rs, c, ks, pb, pbs);
+    lgkm_fence<0>(v8r);
+    if constexpr (RD) lgkm_fence<0>(vr);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const u32x2 ra = vr[(tt * DB + db) * 2], rb = vr[(tt * DB + db) * 2 + 1];
-        const u32x4 av = {ra[0], ra[1], rb[0], rb[1]};
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pb[tt], acc[db], 0, 0, 0);
+        if (db < DB8) {
+          const u32x2 w = v8r[tt * DB8 + db];
+          const u32x4 av = fp8x8_to_bf16(w[0], w[1], 1.0f);
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pbs[tt], acc[db], 0, 0, 0);
+        } else {
+          const int d2 = db - DB8;
+          const u32x2 ra = vr[(tt * 2 + d2) * 2], rb = vr[(tt * 2 + d2) * 2 + 1];
+          const u32x4 av = {ra[0], ra[1], rb[0], rb[1]};
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pb[tt], acc[db], 0, 0, 0);
+        }
       }
   };
 
@@ -305,20 +402,14 @@ __global__ __launch_bounds__(256) void indexed_fp8_mfma(IndexedParams p) {
       else if (younger == 2) wait_vmcnt<2 * kDpb>();
       else if (younger == 1) wait_vmcnt<kDpb>();
       else wait_vmcnt<0>();
-      const uint32_t x = static_cast<uint32_t>(ds_read_i32(list_addr + (j * kBlockKeys + n) * 4));
-      const uint32_t vmask = static_cast<uint32_t>(__ballot(x != kBadRow));  // tile row n's entry is a row
-      const uint32_t zmask = key0 ? static_cast<uint32_t>(__ballot(x == 0u)) : 0u;  // ... and it is row 0
-      if (vmask != 0u) {
-        convert_block(j & (NT - 1));
-        compute(j & (NT - 1), vmask, zmask);
-      }
+      compute(j);
       if (j + NT < nblk) issue_block(j + NT);  // the slot's reads are done (lgkm fences above)
     }
   }
 
   // Epilogue: o = acc / l, lse = ln(2) * (m + log2 l).  Lane (n, h) holds dims 32db + 8j + 4h + {0..3}
-  // of head n.  Each 32-dim block goes through the wave's converted tile area as scaled fp32
-  // (16-byte chunk q of row r at q ^ (r & 7)) and comes back as 8 consecutive dims per lane.
+  // of head n.  Each 32-dim block goes through the wave's first ring slot as scaled fp32 (16-byte
+  // chunk q of row r at q ^ (r & 7)) and comes back as 8 consecutive dims per lane.
   const float l_tot = halves_sum(rs.l);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   const float lse_v = l_tot > 0.0f ? (rs.m * c + log2f(l_tot)) * kLn2 : kNegInf;
@@ -330,14 +421,14 @@ __global__ __launch_bounds__(256) void indexed_fp8_mfma(IndexedParams p) {
     for (int j = 0; j < 4; ++j) {
       const u32x4 w = {__float_as_uint(acc[db][4 * j] * inv), __float_as_uint(acc[db][4 * j + 1] * inv),
                        __float_as_uint(acc[db][4 * j + 2] * inv), __float_as_uint(acc[db][4 * j + 3] * inv)};
-      ds_write_b128<0>(conv_addr + n * 128 + (((2 * j + h) ^ (n & 7)) << 4), w);
+      ds_write_b128<0>(ring_addr + n * 128 + (((2 * j + h) ^ (n & 7)) << 4), w);
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int r = 16 * i + rl;  // head head0 + r
       u32x4 x[2];
-      x[0] = ds_read_b128<0>(conv_addr + r * 128 + (((2 * q4) ^ (r & 7)) << 4));
-      x[1] = ds_read_b128<0>(conv_addr + r * 128 + (((2 * q4 + 1) ^ (r & 7)) << 4));
+      x[0] = ds_read_b128<0>(ring_addr + r * 128 + (((2 * q4) ^ (r & 7)) << 4));
+      x[1] = ds_read_b128<0>(ring_addr + r * 128 + (((2 * q4 + 1) ^ (r & 7)) << 4));
       lgkm_fence<0>(x);
       const int64_t e0 = (row0 + r) * D + 32 * db + 8 * q4;
       if (partial) {

@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256) void indexed_fwd_mfma(IndexedParams p) {
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = lane_id();
-  const int h = lane >> 5;   // half of the wave: which half of head_dim / which key quads
+  const int h = lane >> 5;   // half of the wave: which 8 dims of each MFMA step / which key quads
   const int n = lane & 31;   // key row (A operand) / head (B operand and outputs)
   const int H = p.num_heads, N = p.kv_len, K = p.topk;
   const int n_hg = H / 32;
@@ -85,12 +85,14 @@ __global__ __launch_bounds__(256) void indexed_fwd_mfma(IndexedParams p) {
   const bool key0 = p.sink_mode == kSinkKey0;
   const bool null_sink = !kMass && !partial && p.sink_mode == kSinkNull;
 
-  // B operand of S^T: q[bt, head0 + n, h*D/2 + 8s .. +8] (logical chunk h*S + s of the row).
+  // B operand of S^T: q[bt, head0 + n, 16s + 8h .. +8] (logical chunk 2s + h of the row).  MFMA
+  // step s sums dims 16s .. 16s + 15; the fp8-cache kernel uses the same steps, so that both sum
+  // a row's products in one order.
   bf16x8 qf[S];
   {
-    const __bf16 *qrow = static_cast<const __bf16 *>(p.q) + (bt * H + head0 + n) * D + h * (D / 2);
+    const __bf16 *qrow = static_cast<const __bf16 *>(p.q) + (bt * H + head0 + n) * D + 8 * h;
 #pragma unroll
-    for (int s = 0; s < S; ++s) qf[s] = *reinterpret_cast<const bf16x8 *>(qrow + s * 8);
+    for (int s = 0; s < S; ++s) qf[s] = *reinterpret_cast<const bf16x8 *>(qrow + s * 16);
   }
   const float c = p.scale_log2;  // > 0 on this path
   const float sink_raw = p.sinks ? p.sinks[head0 + n] * kLog2e / c : 0.0f;  // raw logit units
@@ -148,9 +150,9 @@ __global__ __launch_bounds__(256) void indexed_fwd_mfma(IndexedParams p) {
   };
 
   // LDS operand addresses (bits 4..7 of every tile base are clear, see the window kernel):
-  // K rows: row n, logical chunk h*S + s at kbase ^ 16 s; V^T quads at vbase ^ (64 db + 16 e) plus
+  // K rows: row n, logical chunk 2s + h at kbase ^ 32 s; V^T quads at vbase ^ (64 db + 16 e) plus
   // rows 8 e + 16 tt.
-  const uint32_t kbase = ring_addr + Tile::offset(n, h * S);
+  const uint32_t kbase = ring_addr + Tile::offset(n, h);
   uint32_t vbase;
   {
     const int g16 = lane >> 4, i16 = lane & 15;
@@ -164,7 +166,7 @@ __global__ __launch_bounds__(256) void indexed_fwd_mfma(IndexedParams p) {
     asm volatile("" : "+v"(kb_));
     u32x4 kf[S];
 #pragma unroll
-    for (int s = 0; s < S; ++s) kf[s] = ds_read_b128<0>(kb_ ^ (16u * s));
+    for (int s = 0; s < S; ++s) kf[s] = ds_read_b128<0>(kb_ ^ (32u * s));
     lgkm_fence<0>(kf);
     f32x16 st = f32x16{};
 #pragma unroll
