@@ -28,7 +28,9 @@
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library
  *     allocates nothing, keeps no pointer after returning and holds no mutable
- *     global state, so it may be called from several host threads.
+ *     global state, so it may be called from several host threads.  The one
+ *     exception is sattn_indexed_fwd_noalloc, whose split-K partials live in a
+ *     fixed device array per GPU (see its declaration).
  *   - Every kernel is enqueued on `stream` (the split-K merge included);
  *     nothing runs on the default stream unless `stream` is it, and nothing
  *     synchronises.  A caller that produces inputs on another stream must make
@@ -42,6 +44,11 @@
  *     must be 16-byte aligned and head_dim a multiple of 8.
  *   - Output rows whose key set is empty get o = 0 and lse = -inf (with a null
  *     sink: lse = sinks[h]).
+ *
+ * Tracing: with SATTN_TRACE set to a value other than "" or "0" when the
+ * library first looks at it, every kernel launch prints one line to stderr,
+ * "[sattn] <kernel variant> grid=... block=... (<the sizes that chose it>)",
+ * before the launch is enqueued.
  */
 #ifndef SATTN_H
 #define SATTN_H
