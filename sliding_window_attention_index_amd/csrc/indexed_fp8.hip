@@ -327,9 +327,9 @@ __global__ __launch_bounds__(256) void indexed_fp8_mfma(IndexedParams p) {
       for (int d2 = 0; d2 < 2; ++d2) {
         const uint32_t dx = 64u * d2;
         vr[d2 * 2] = ds_read_tr_b16<0>(vb ^ dx);
-        vr[d2 * 2 + 1] = ds_read_tr_b16<kRow8>(vb ^ (dx + 16u));
+        vr[d2 * 2 + 1] = ds_read_tr_b16<kRow8>(vb ^ (dx + T64::kRow8Xor));
         vr[4 + d2 * 2] = ds_read_tr_b16<2 * kRow8>(vb ^ dx);
-        vr[4 + d2 * 2 + 1] = ds_read_tr_b16<3 * kRow8>(vb ^ (dx + 16u));
+        vr[4 + d2 * 2 + 1] = ds_read_tr_b16<3 * kRow8>(vb ^ (dx + T64::kRow8Xor));
       }
     }
     // Accumulator element r of lane (n, h) is key 8*(r/4) + 4h + r%4 of head n.

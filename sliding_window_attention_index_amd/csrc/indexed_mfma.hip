@@ -150,7 +150,7 @@ __global__ __launch_bounds__(256) void indexed_fwd_mfma(IndexedParams p) {
   };
 
   // LDS operand addresses (bits 4..7 of every tile base are clear, see the window kernel):
-  // K rows: row n, logical chunk 2s + h at kbase ^ 32 s; V^T quads at vbase ^ (64 db + 16 e) plus
+  // K rows: row n, logical chunk 2s + h at kbase ^ 32 s; V^T quads at vbase ^ (64 db + 32 e) plus
   // rows 8 e + 16 tt.
   const uint32_t kbase = ring_addr + Tile::offset(n, h);
   uint32_t vbase;
@@ -189,9 +189,9 @@ __global__ __launch_bounds__(256) void indexed_fwd_mfma(IndexedParams p) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         vr[db * 2] = ds_read_tr_b16<0>(vb ^ (64u * db));
-        vr[db * 2 + 1] = ds_read_tr_b16<kRow8>(vb ^ (64u * db + 16u));
+        vr[db * 2 + 1] = ds_read_tr_b16<kRow8>(vb ^ (64u * db + Tile::kRow8Xor));
         vr[2 * DB + db * 2] = ds_read_tr_b16<2 * kRow8>(vb ^ (64u * db));
-        vr[2 * DB + db * 2 + 1] = ds_read_tr_b16<3 * kRow8>(vb ^ (64u * db + 16u));
+        vr[2 * DB + db * 2 + 1] = ds_read_tr_b16<3 * kRow8>(vb ^ (64u * db + Tile::kRow8Xor));
       }
       // Accumulator element r of lane (n, h) is key 8*(r/4) + 4h + r%4 of head n.
       if (zmask) bias_block(st, zmask, h, sink_raw);

@@ -125,7 +125,7 @@ __global__ __launch_bounds__(256, 2) void indexed_slice_mfma(IndexedParams p) {
   const uint32_t mask_addr = lds_addr(&tmask[0][0]);
 
   // LDS operand addresses (bits 4..7 of every tile base are clear): K rows: row n, logical chunk
-  // h*S + s at kbase ^ 16 s; V^T quads at vbase ^ (64 db + 16 e) plus rows 8 e + 16 tt.
+  // h*S + s at kbase ^ 16 s; V^T quads at vbase ^ (64 db + 32 e) plus rows 8 e + 16 tt.
   const uint32_t kbase = ring_addr + Tile::offset(n, h * S);
   uint32_t vbase;
   {
@@ -157,9 +157,9 @@ __global__ __launch_bounds__(256, 2) void indexed_slice_mfma(IndexedParams p) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       vr[db * 2] = ds_read_tr_b16<0>(vb ^ (64u * db));
-      vr[db * 2 + 1] = ds_read_tr_b16<kRow8>(vb ^ (64u * db + 16u));
+      vr[db * 2 + 1] = ds_read_tr_b16<kRow8>(vb ^ (64u * db + Tile::kRow8Xor));
       vr[2 * DB + db * 2] = ds_read_tr_b16<2 * kRow8>(vb ^ (64u * db));
-      vr[2 * DB + db * 2 + 1] = ds_read_tr_b16<3 * kRow8>(vb ^ (64u * db + 16u));
+      vr[2 * DB + db * 2 + 1] = ds_read_tr_b16<3 * kRow8>(vb ^ (64u * db + Tile::kRow8Xor));
     }
     if (zmask) bias_block(st, zmask, h, sink_raw);
     if (vmask != 0xffffffffu) mask_block(st, vmask, h);

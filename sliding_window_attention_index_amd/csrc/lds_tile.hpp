@@ -27,11 +27,24 @@ struct SwizzledTile {
   static constexpr int kBytes = kRows * kRowBytes;
   static constexpr int kDmaPerTile = kBytes / 1024;  // wave-wide DMA instructions per tile
 
-  // Physical chunk of logical chunk c in row r.
+  // Physical chunk of logical chunk c in row r: c ^ f(r).  The LDS serves 256 bytes (64 banks of
+  // 4 bytes) a clock: a 16-byte read of 64 lanes goes 16 lanes at a time, an 8-byte read 32 lanes at
+  // a time.  f is chosen so that both of these are conflict free:
+  //   * 16 consecutive rows (16k .. 16k + 15) reading one logical chunk (the K operand): f takes
+  //     distinct values on the rows of the group that share a 256-byte bank window position;
+  //   * 4 consecutive rows (4k .. 4k + 3) reading an aligned run of 4 chunks with
+  //     ds_read_b64_tr_b16 (the V^T operand, 32 lanes = 4 rows x 4 chunks x 8 bytes): the rows
+  //     that share bank positions differ in bit 2 of f, so their chunk runs do not overlap.
+  // D = 128 (256-byte rows): f(r) = 4 (r % 4) + (r / 4) % 4.  D = 64 (128-byte rows, two to a bank
+  // window, even and odd rows on opposite halves): f(r) = 4 ((r / 2) % 2) + (r / 4) % 4.
   __device__ static __forceinline__ int phys(int r, int c) {
-    if constexpr (D == 128) return c ^ (((r & 7) << 1) | ((r >> 3) & 1));
-    else return c ^ ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
+    if constexpr (D == 128) return c ^ (((r & 3) << 2) | ((r >> 2) & 3));
+    else return c ^ ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
   }
+  // f(r + 8) = f(r) ^ 2 and f(r + 16) = f(r): a read 8 rows further (an immediate offset of
+  // 8 rows) finds logical chunk c at the address of chunk c ^ 2 of its own row, i.e. the byte
+  // address XORed with kRow8Xor; 16 rows further, at the same address.
+  static constexpr uint32_t kRow8Xor = 32;
   // Byte offset inside the tile of logical chunk c of row r.
   __device__ static __forceinline__ int offset(int r, int c) { return r * kRowBytes + phys(r, c) * 16; }
 

@@ -161,7 +161,7 @@ __global__ __launch_bounds__(256, D == 128 && (G <= 4 || G == 32) ? 3 : 1) void 
 
   // ---- per-lane LDS read addresses of the K rows (A operand) and V^T quads.  XOR addressing (D = 128;
   // bits 4..7 of every tile base are clear): row n's logical chunk h S + s at kbase ^ 16 s, V^T quads
-  // at vbase ^ (64 db + 16 e) plus rows 8 e + 16 tt.  Otherwise one precomputed register per read
+  // at vbase ^ (64 db + 32 e) plus rows 8 e + 16 tt.  Otherwise one precomputed register per read
   // (koff, voff). ----
   const uint32_t ring_addr = lds_addr(ring);
   const int g16 = lane >> 4, i16 = lane & 15;
@@ -219,9 +219,9 @@ __global__ __launch_bounds__(256, D == 128 && (G <= 4 || G == 32) ? 3 : 1) void 
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         vr[db * 2] = ds_read_tr_b16<off>(vb ^ (64u * db));
-        vr[db * 2 + 1] = ds_read_tr_b16<off + kRow8>(vb ^ (64u * db + 16u));
+        vr[db * 2 + 1] = ds_read_tr_b16<off + kRow8>(vb ^ (64u * db + Tile::kRow8Xor));
         vr[2 * DB + db * 2] = ds_read_tr_b16<off + 2 * kRow8>(vb ^ (64u * db));
-        vr[2 * DB + db * 2 + 1] = ds_read_tr_b16<off + 3 * kRow8>(vb ^ (64u * db + 16u));
+        vr[2 * DB + db * 2 + 1] = ds_read_tr_b16<off + 3 * kRow8>(vb ^ (64u * db + Tile::kRow8Xor));
       }
     } else {
 #pragma unroll
