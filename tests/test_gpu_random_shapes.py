@@ -123,3 +123,49 @@ def test_window_random_shapes(dev, spec):
     case = W.make_window_case(name, lens, H, Hkv, D, wl, wr, mode, dtype=dt, seed=seed % 1000)
     r = check_window(case, dev)
     print(f"[parity] {name}: {r}", flush=True)
+
+
+def _fp8_specs(n_cases, seed):
+    rng = np.random.default_rng(seed)
+    specs = []
+    for i in range(n_cases):
+        H = int(rng.choice([32, 64, 96]))
+        rd = int(rng.choice([0, 64]))
+        big = i % 5 == 4  # 4096 or more (query, head group, slice) tasks: the 2-slot ring
+        B = 2 if big else int(rng.integers(1, 3))
+        M = int(rng.integers(1100, 1400)) if big else int(rng.choice([1, 3, 17, 130]))
+        N = int(rng.integers(1, 2000))
+        K = int(rng.integers(1, 40)) if big else int(rng.integers(1, 600))
+        splits = int(rng.choice([1, 1, 2, 3, 8]))
+        mode = int(rng.integers(0, 3))
+        specs.append((f"fp8_{i}_b{B}m{M}h{H}rd{rd}n{N}k{K}s{splits}_{SINK_NAMES[mode]}",
+                      B, M, H, rd, N, K, splits, mode, int(rng.integers(0, 2**31))))
+    return specs
+
+
+FP8 = _fp8_specs(20, 99)
+
+
+@pytest.mark.parametrize("spec", FP8, ids=[s[0] for s in FP8])
+def test_indexed_fp8_random_shapes(dev, spec):
+    """The fp8 cache entry point on the same kind of lists, unit-scale rows (the bf16 bar's
+    reading: the probabilities' rounding stays within it while |v| is near |o|)."""
+    import sliding_window_attention_index_amd as sattn
+    from oracle import fp8_cache as F8
+    from parity import compare
+    name, B, M, H, rd, N, K, splits, mode, seed = spec
+    rng = np.random.default_rng(seed)
+    kv8, sc, rope = W.fp8_cache(seed % 1000, B, N, 128, rd, scale_spread=0)
+    g = torch.Generator().manual_seed(seed % 1000 + 1)
+    q = torch.randn(B, M, H, 128, generator=g).to(torch.bfloat16)
+    sinks = torch.randn(H, generator=g)
+    idx = torch.from_numpy(_lists(rng, B, M, N, K))
+    o, lse = sattn.indexed_fp8_fwd(q.to(dev), kv8.to(dev), sc.to(dev), rope.to(dev) if rd else None, idx.to(dev),
+                                   sinks=sinks.to(dev) if mode else None, sink_mode=SINK_NAMES[mode],
+                                   num_splits=splits, return_lse=True)
+    torch.cuda.synchronize(dev)
+    o_ref, l_ref = F8.indexed_fp8(q, kv8, sc, rope if rd else None, idx, softmax_scale=128 ** -0.5,
+                                  sinks=sinks, sink_mode=mode)
+    e = compare(o, o_ref, torch.bfloat16, f"{name} o")
+    compare(lse, l_ref, torch.bfloat16, f"{name} lse", lse=True)
+    print(f"[parity] {name}: max_abs {e:.3e}", flush=True)
