@@ -428,7 +428,8 @@ sattn_status sattn_merge_lse(const sattn_merge_args *args, hipStream_t stream);
  *   - Calls whose partials need more than the scratch
  *     (sattn_indexed_workspace_size(...) > SATTN_NOALLOC_SCRATCH_BYTES) return
  *     SATTN_ERR_SCRATCH_LIMIT before anything is enqueued.
- *   - The scratch of the current device (hipGetDevice) is used; `stream` must belong to it.
+ *   - The scratch of the current device (hipGetDevice) is used; `stream` must belong to it
+ *     (a stream of another device returns SATTN_ERR_UNSUPPORTED before anything is enqueued).
  *   - Every call on one GPU shares that GPU's scratch: calls that overlap on one GPU (on
  *     different streams, or from several host threads without ordering) race and give wrong
  *     results.  Calls ordered on one stream do not.

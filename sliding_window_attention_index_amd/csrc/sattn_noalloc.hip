@@ -29,7 +29,7 @@ struct DeviceScratch {
 DeviceScratch g_scratch[kMaxDevices];
 
 // Device address of this device's copy of `scratch`, looked up at the first call on the device.
-void *scratch_on_current_device(sattn_status *st) {
+void *scratch_on_current_device(hipStream_t stream, sattn_status *st) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) {
     *st = SATTN_ERR_LAUNCH;
@@ -38,6 +38,15 @@ void *scratch_on_current_device(sattn_status *st) {
   if (dev < 0 || dev >= kMaxDevices) {
     *st = SATTN_ERR_UNSUPPORTED;
     return nullptr;
+  }
+  // The scratch address is the current device's: a stream of another device would hand its
+  // kernels an address that is not theirs.
+  if (stream != nullptr) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess || sdev != dev) {
+      *st = SATTN_ERR_UNSUPPORTED;
+      return nullptr;
+    }
   }
   DeviceScratch &d = g_scratch[dev];
   std::call_once(d.once, [&d]() { d.err = hipGetSymbolAddress(&d.ptr, HIP_SYMBOL(scratch)); });
@@ -58,7 +67,7 @@ extern "C" sattn_status sattn_indexed_fwd_noalloc(const sattn_indexed_args *a, h
     return SATTN_ERR_SCRATCH_LIMIT;  // before the device is touched
   if (a->num_splits <= 1) return sattn::indexed_fwd_with_workspace(a, nullptr, 0, stream);
   sattn_status st;
-  void *ws = scratch_on_current_device(&st);
+  void *ws = scratch_on_current_device(stream, &st);
   if (!ws) return st;
   return sattn::indexed_fwd_with_workspace(a, ws, kScratchBytes, stream);
 }
