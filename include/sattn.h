@@ -381,8 +381,9 @@ sattn_status sattn_indexer_topk(const sattn_indexer_args *args, hipStream_t stre
  *             sattn_indexed_args with dtype bf16 (the workspace size is the same)
  *   kv_fp8    [batch, kv_len, head_dim - rope_dims] uint8: e4m3 codes (OCP "fn": bias 7, no
  *             infinities; S.1111.111 is NaN) of the first head_dim - rope_dims dims of each row
- *   kv_scale  [batch, kv_len] fp32: one power-of-two scale per row (other values act as the
- *             power of two of their exponent); row value = e4m3(code) * scale
+ *   kv_scale  [batch, kv_len] fp32: one scale per row, a positive power of two (the keys take
+ *             only its exponent, the values its whole value: other scales are not supported and
+ *             give unspecified results); row value = e4m3(code) * scale
  *   kv_rope   [batch, kv_len, rope_dims] bf16: the last rope_dims dims of each row (NULL when
  *             rope_dims is 0)
  *   head_dim  128; rope_dims 0 or 64; num_heads a multiple of 32; softmax_scale > 0
