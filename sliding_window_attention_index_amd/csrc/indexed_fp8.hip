@@ -80,6 +80,13 @@ __device__ __forceinline__ u32x2 ds_read_b64(uint32_t addr) {
   return r;
 }
 
+template <int OFF>
+__device__ __forceinline__ uint32_t ds_read_b32_off(uint32_t addr) {
+  uint32_t r;
+  asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+
 // Eight LDS bytes per lane, transposed across lanes: in each group of 16 lanes, lane i receives as
 // its byte e (e = 0..7) byte i % 8 of the 8 bytes that lane 2e + i / 8 of the group addresses.
 template <int OFF>
@@ -117,6 +124,11 @@ __device__ __forceinline__ void softmax_probs_scaled(const f32x16 &st, RowSoftma
   }
   rs.l += l0 + l1;
 }
+
+template <int I>
+struct Slot {
+  static constexpr int value = I;
+};
 
 template <int RD, int NT>
 __global__ __launch_bounds__(256) void indexed_fp8_mfma(IndexedParams p) {
@@ -260,38 +272,43 @@ __global__ __launch_bounds__(256) void indexed_fp8_mfma(IndexedParams p) {
   constexpr int kRow8 = 8 * T64::kRowBytes;
   constexpr int kRows16 = 16 * D8;  // 16 fp8 rows (the same swizzle)
 
-  // Block j from its slot: row n's list entry is read with the block's operands, and a block
-  // without a row is skipped once it is known.
-  auto compute = [&](int j) {
-    const uint32_t sb = ring_addr + (j & (NT - 1)) * kSlotBytes;
+  // Every LDS operand address of a block, computed once for slot 0 (the XORed chunk addresses in
+  // registers); the slot is the reads' immediate offset (the block loop runs over compile-time
+  // slots).
+  constexpr int kS8 = D8 / 16;  // MFMA steps over fp8 dims
+  constexpr int kSR = S - kS8 > 0 ? S - kS8 : 1;
+  uint32_t a_k8[kS8], a_kr[kSR], a_v8[DB8], a_vr[2][2];
+#pragma unroll
+  for (int s = 0; s < kS8; ++s) a_k8[s] = (ring_addr + k8) ^ (16u * s);
+#pragma unroll
+  for (int s = 0; s < kSR; ++s) a_kr[s] = (ring_addr + kr) ^ (32u * s);
+  const uint32_t a_ks = ring_addr + kScaleOff + 4 * n, a_ps = ring_addr + kScaleOff + 16 * h;
+#pragma unroll
+  for (int db = 0; db < DB8; ++db) a_v8[db] = (ring_addr + v8) ^ (32u * db);
+#pragma unroll
+  for (int d2 = 0; d2 < 2; ++d2) {
+    a_vr[d2][0] = (ring_addr + voff) ^ (64u * d2);
+    a_vr[d2][1] = (ring_addr + voff) ^ (64u * d2 + T64::kRow8Xor);
+  }
+
+  auto compute = [&](auto I, int j) {
+    constexpr int so = decltype(I)::value * kSlotBytes;  // the slot's byte offset
     // K operand and the scales: this lane's row (K) and its keys' (probabilities).
-    constexpr int kS8 = D8 / 16;  // MFMA steps over fp8 dims
     u32x2 k8r[kS8];
-    u32x4 krr[S - kS8 > 0 ? S - kS8 : 1];
-    {
-      uint32_t ka = sb + k8;
-      asm volatile("" : "+v"(ka));
+    u32x4 krr[kSR];
 #pragma unroll
-      for (int s = 0; s < kS8; ++s) k8r[s] = ds_read_b64<0>(ka ^ (16u * s));
-    }
+    for (int s = 0; s < kS8; ++s) k8r[s] = ds_read_b64<so>(a_k8[s]);
     if constexpr (RD) {
-      uint32_t ka = sb + kr;
-      asm volatile("" : "+v"(ka));
 #pragma unroll
-      for (int s = 0; s < S - kS8; ++s) krr[s] = ds_read_b128<0>(ka ^ (32u * s));
+      for (int s = 0; s < S - kS8; ++s) krr[s] = ds_read_b128<so>(a_kr[s]);
     }
-    const uint32_t scb = sb + kScaleOff;
     int ksb[1];
-    ksb[0] = static_cast<int>(ds_read_b32_raw(scb + 4 * n));
+    ksb[0] = static_cast<int>(ds_read_b32_off<so>(a_ks));
     u32x4 ks[4];
-    {
-      uint32_t pa = scb + 16 * h;
-      asm volatile("" : "+v"(pa));
-      ks[0] = ds_read_b128<0>(pa);
-      ks[1] = ds_read_b128<32>(pa);
-      ks[2] = ds_read_b128<64>(pa);
-      ks[3] = ds_read_b128<96>(pa);
-    }
+    ks[0] = ds_read_b128<so>(a_ps);
+    ks[1] = ds_read_b128<so + 32>(a_ps);
+    ks[2] = ds_read_b128<so + 64>(a_ps);
+    ks[3] = ds_read_b128<so + 96>(a_ps);
     uint32_t xr[1];
     xr[0] = ds_read_b32_raw(list_addr + (j * kBlockKeys + n) * 4);
     lgkm_fence<0>(k8r);
@@ -310,26 +327,21 @@ __global__ __launch_bounds__(256) void indexed_fp8_mfma(IndexedParams p) {
       st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf), qf[s], st, 0, 0, 0);
     }
     // V^T operands.
-    uint32_t va = sb + v8;
-    asm volatile("" : "+v"(va));
     u32x2 v8r[2 * DB8];
 #pragma unroll
     for (int db = 0; db < DB8; ++db) {
-      v8r[db] = ds_read_tr_b8<0>(va ^ (32u * db));
-      v8r[DB8 + db] = ds_read_tr_b8<kRows16>(va ^ (32u * db));
+      v8r[db] = ds_read_tr_b8<so>(a_v8[db]);
+      v8r[DB8 + db] = ds_read_tr_b8<so + kRows16>(a_v8[db]);
     }
     constexpr int kV16 = RD ? 8 : 1;
     u32x2 vr[kV16];
     if constexpr (RD) {
-      uint32_t vb = sb + voff;
-      asm volatile("" : "+v"(vb));
 #pragma unroll
       for (int d2 = 0; d2 < 2; ++d2) {
-        const uint32_t dx = 64u * d2;
-        vr[d2 * 2] = ds_read_tr_b16<0>(vb ^ dx);
-        vr[d2 * 2 + 1] = ds_read_tr_b16<kRow8>(vb ^ (dx + T64::kRow8Xor));
-        vr[4 + d2 * 2] = ds_read_tr_b16<2 * kRow8>(vb ^ dx);
-        vr[4 + d2 * 2 + 1] = ds_read_tr_b16<3 * kRow8>(vb ^ (dx + T64::kRow8Xor));
+        vr[d2 * 2] = ds_read_tr_b16<so>(a_vr[d2][0]);
+        vr[d2 * 2 + 1] = ds_read_tr_b16<so + kRow8>(a_vr[d2][1]);
+        vr[4 + d2 * 2] = ds_read_tr_b16<so + 2 * kRow8>(a_vr[d2][0]);
+        vr[4 + d2 * 2 + 1] = ds_read_tr_b16<so + 3 * kRow8>(a_vr[d2][1]);
       }
     }
     // Accumulator element r of lane (n, h) is key 8*(r/4) + 4h + r%4 of head n.
@@ -395,15 +407,26 @@ __global__ __launch_bounds__(256) void indexed_fp8_mfma(IndexedParams p) {
 #pragma unroll
     for (int j = 0; j < NT; ++j)
       if (j < nblk) issue_block(j);
-    for (int j = 0; j < nblk; ++j) {
+    auto step = [&](auto I, int j) {  // block j, in ring slot I = j % NT
       // This wave's DMAs younger than block j's: those of the next min(NT - 1, nblk - 1 - j) blocks.
       const int younger = min(NT - 1, nblk - 1 - j);
       if (younger == 3) wait_vmcnt<3 * kDpb>();
       else if (younger == 2) wait_vmcnt<2 * kDpb>();
       else if (younger == 1) wait_vmcnt<kDpb>();
       else wait_vmcnt<0>();
-      compute(j);
+      compute(I, j);
       if (j + NT < nblk) issue_block(j + NT);  // the slot's reads are done (lgkm fences above)
+    };
+    for (int j = 0; j < nblk; j += NT) {
+      step(Slot<0>{}, j);
+      if (j + 1 >= nblk) break;
+      step(Slot<1>{}, j + 1);
+      if constexpr (NT == 4) {
+        if (j + 2 >= nblk) break;
+        step(Slot<2>{}, j + 2);
+        if (j + 3 >= nblk) break;
+        step(Slot<3>{}, j + 3);
+      }
     }
   }
 

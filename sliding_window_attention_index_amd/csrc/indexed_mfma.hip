@@ -56,6 +56,11 @@ __device__ __forceinline__ int ds_read_i32(uint32_t addr) {
   return r;
 }
 
+template <int I>
+struct Slot {
+  static constexpr int value = I;
+};
+
 template <int D, int NT, bool kMass>
 __global__ __launch_bounds__(256) void indexed_fwd_mfma(IndexedParams p) {
   using Tile = SwizzledTile<D>;
@@ -160,13 +165,32 @@ __global__ __launch_bounds__(256) void indexed_fwd_mfma(IndexedParams p) {
     vbase = ring_addr + Tile::offset(4 * h + (i16 >> 2), c2) + (i16 & 1) * 8;
   }
   constexpr int kRow8 = 8 * Tile::kRowBytes;
-
-  auto compute = [&](int slot, uint32_t vmask, uint32_t zmask) {
-    uint32_t kb_ = kbase + slot * Tile::kBytes;  // opaque per block: the XORed addresses stay local
-    asm volatile("" : "+v"(kb_));
-    u32x4 kf[S];
+  // Every LDS operand address of a block, computed once: the XORed chunk addresses of slot 0 in
+  // registers (this kernel has registers to spare at two waves per SIMD), the slot as the reads'
+  // immediate offset (the block loop runs over compile-time slots).
+  uint32_t kaddr[kMass ? 1 : S], vaddr[DB][2];
 #pragma unroll
-    for (int s = 0; s < S; ++s) kf[s] = ds_read_b128<0>(kb_ ^ (32u * s));
+  for (int s = 0; s < (kMass ? 1 : S); ++s) kaddr[s] = kbase ^ (32u * s);
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    vaddr[db][0] = vbase ^ (64u * db);
+    vaddr[db][1] = vbase ^ (64u * db + Tile::kRow8Xor);
+  }
+
+  // Block in ring slot I (attention: compile-time) or `slot` (block mass, which keeps one
+  // address register and XORs at every block: there the unrolled slot loop measured slower).
+  auto compute = [&](auto I, int slot, uint32_t vmask, uint32_t zmask) {
+    constexpr int off = decltype(I)::value * Tile::kBytes;
+    u32x4 kf[S];
+    if constexpr (kMass) {
+      uint32_t kb_ = kbase + slot * Tile::kBytes;  // opaque per block: the XORed addresses stay local
+      asm volatile("" : "+v"(kb_));
+#pragma unroll
+      for (int s = 0; s < S; ++s) kf[s] = ds_read_b128<0>(kb_ ^ (32u * s));
+    } else {
+#pragma unroll
+      for (int s = 0; s < S; ++s) kf[s] = ds_read_b128<off>(kaddr[s]);
+    }
     lgkm_fence<0>(kf);
     f32x16 st = f32x16{};
 #pragma unroll
@@ -183,15 +207,13 @@ __global__ __launch_bounds__(256) void indexed_fwd_mfma(IndexedParams p) {
       }
       bin_sum += e0 + e1;
     } else {
-      uint32_t vb = vbase + slot * Tile::kBytes;
-      asm volatile("" : "+v"(vb));
       u32x2 vr[4 * DB];
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        vr[db * 2] = ds_read_tr_b16<0>(vb ^ (64u * db));
-        vr[db * 2 + 1] = ds_read_tr_b16<kRow8>(vb ^ (64u * db + Tile::kRow8Xor));
-        vr[2 * DB + db * 2] = ds_read_tr_b16<2 * kRow8>(vb ^ (64u * db));
-        vr[2 * DB + db * 2 + 1] = ds_read_tr_b16<3 * kRow8>(vb ^ (64u * db + Tile::kRow8Xor));
+        vr[db * 2] = ds_read_tr_b16<off>(vaddr[db][0]);
+        vr[db * 2 + 1] = ds_read_tr_b16<off + kRow8>(vaddr[db][1]);
+        vr[2 * DB + db * 2] = ds_read_tr_b16<off + 2 * kRow8>(vaddr[db][0]);
+        vr[2 * DB + db * 2 + 1] = ds_read_tr_b16<off + 3 * kRow8>(vaddr[db][1]);
       }
       // Accumulator element r of lane (n, h) is key 8*(r/4) + 4h + r%4 of head n.
       if (zmask) bias_block(st, zmask, h, sink_raw);
@@ -271,7 +293,7 @@ __global__ __launch_bounds__(256) void indexed_fwd_mfma(IndexedParams p) {
 #pragma unroll
     for (int j = 0; j < NT; ++j)
       if (j < nblk) issue_block(j);
-    for (int j = 0; j < nblk; ++j) {
+    auto step = [&](auto I, int j) {  // block j, in ring slot I = j % NT
       // This wave's DMAs younger than block j's: those of the next min(NT - 1, nblk - 1 - j) blocks.
       const int younger = min(NT - 1, nblk - 1 - j);
       if (younger == 3) wait_vmcnt<3 * kDpb>();
@@ -281,7 +303,7 @@ __global__ __launch_bounds__(256) void indexed_fwd_mfma(IndexedParams p) {
       const uint32_t x = static_cast<uint32_t>(ds_read_i32(list_addr + (j * kBlockKeys + entry_of_row(n)) * 4));
       const uint32_t vmask = static_cast<uint32_t>(__ballot(x != kBadRow));  // tile row n's entry is a row
       const uint32_t zmask = key0 ? static_cast<uint32_t>(__ballot(x == 0u)) : 0u;  // ... and it is row 0
-      if (vmask != 0u) compute(j & (NT - 1), vmask, zmask);
+      if (vmask != 0u) compute(I, j & (NT - 1), vmask, zmask);
       if constexpr (kMass) {
         if (--bin_left == 0 || (j == nblk - 1 && cend == ke)) {  // the block ends with this tile
           const float tot = halves_sum(bin_sum);
@@ -293,6 +315,21 @@ __global__ __launch_bounds__(256) void indexed_fwd_mfma(IndexedParams p) {
         }
       }
       if (j + NT < nblk) issue_block(j + NT);  // the slot's reads are done (lgkm fences in compute)
+    };
+    if constexpr (kMass) {
+      for (int j = 0; j < nblk; ++j) step(Slot<0>{}, j);
+    } else {
+      for (int j = 0; j < nblk; j += NT) {
+        step(Slot<0>{}, j);
+        if (j + 1 >= nblk) break;
+        step(Slot<1>{}, j + 1);
+        if constexpr (NT == 4) {
+          if (j + 2 >= nblk) break;
+          step(Slot<2>{}, j + 2);
+          if (j + 3 >= nblk) break;
+          step(Slot<3>{}, j + 3);
+        }
+      }
     }
   }
 
