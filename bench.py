@@ -29,6 +29,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -43,11 +44,47 @@ BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def _src_hash() -> str:
+# The kernel sources each workload's timed launches are built from (the host dispatch in
+# sattn_api.cpp and every csrc/ header these include are added; the public header, declarations and
+# their documentation, is not): counters taken of a workload stay valid while these files are
+# unchanged.
+KERNEL_SOURCES = {
+    "vision_window": ["window_mfma.hip"],
+    "causal_window_null": ["window_mfma.hip"],
+    "sparse_prefill": ["indexed_mfma.hip"],
+    "sparse_prefill_block_mass": ["indexed_mfma.hip"],
+    "sparse_decode": ["indexed_slice.hip", "valu_fwd.hip"],
+    "sparse_prefill_fp8": ["indexed_fp8.hip"],
+    "sparse_decode_fp8": ["indexed_fp8.hip", "valu_fwd.hip"],
+    "topk_idx_build": ["index_build.hip"],
+    "compress_pool": ["compress.hip"],
+    "indexer_topk": ["indexer.hip"],
+}
+_CSRC = os.path.join(ROOT, "sliding_window_attention_index_amd", "csrc")
+
+
+def _with_includes(names):
+    """The csrc/ files and, transitively, the csrc/ headers they include."""
+    seen, todo = [], list(names)
+    while todo:
+        n = todo.pop()
+        if n in seen:
+            continue
+        path = os.path.join(_CSRC, n)
+        if not os.path.exists(path):
+            continue
+        seen.append(n)
+        with open(path) as f:
+            todo += re.findall(r'^\s*#include\s+"([^"]+)"', f.read(), flags=re.M)
+    return sorted(seen)
+
+
+def _src_hash(workload: str | None = None) -> str:
+    """Hash of the kernel sources: of every csrc/ file, or of those a workload's launches use."""
+    names = sorted(os.listdir(_CSRC)) if workload is None else _with_includes(KERNEL_SOURCES[workload] + ["sattn_api.cpp"])
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "sliding_window_attention_index_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
+    for name in names:
+        with open(os.path.join(_CSRC, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
@@ -61,7 +98,7 @@ def _counters(workload: str):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha") != _src_hash():
+    if rec.get("kernel_source_sha") != _src_hash(workload):
         return None
     return rec
 
