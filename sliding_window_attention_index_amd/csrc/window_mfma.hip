@@ -10,7 +10,7 @@
 //
 // gfx950 mapping:
 //   * One workgroup per tile = (KV head g, QT consecutive queries of one
-//     sequence).  Each of its 4 waves owns 32 rows = 32/G queries x G heads
+//     sequence).  Each of its waves (4 at D = 128, 8 at D = 64) owns 32 rows = 32/G queries x G heads
 //     (the G query heads of one KV head share every K/V element, so they fill
 //     the MFMA N dimension) and keeps their Q operand in registers.  The tile
 //     walks the 32-key blocks that meet the band of any of its queries; a
@@ -21,11 +21,12 @@
 //     L2.
 //   * K and V blocks arrive by direct global->LDS DMA (buffer_load ... lds)
 //     into a ring of swizzled slots (K tile + V tile; 3 slots at D = 128, so
-//     that three workgroups share a CU, 4 at D = 64) shared by the four
-//     waves; each wave fetches a quarter of every slot.  Block j + slots - 1
-//     is requested while block j is computed.  Requests past the last block
-//     point outside the buffer (they move no data), so every step waits for
-//     the same number of this wave's requests; one barrier per step then
+//     that three workgroups share a CU, 4 at D = 64) shared by the
+//     workgroup's waves; each wave fetches an equal share of every slot.
+//     Block j + slots - 1 is requested while block j is computed.  Requests
+//     past the last block point outside the buffer (they read no memory and
+//     land as zeros in a slot no step reads), so every step waits for the
+//     same number of this wave's requests; one barrier per step then
 //     publishes the slot and frees the one read in the step before.
 //   * LDS reads are inline asm the compiler cannot see, so it never inserts
 //     a full vmcnt(0) wait for them; lgkmcnt waits are explicit.
@@ -52,8 +53,17 @@ struct Idx {
   static constexpr int value = I;
 };
 
+// Waves per workgroup.  D = 64 (four waves per SIMD) runs workgroups of eight waves, two to a CU, so
+// that each staged K/V block serves twice the queries of a four-wave tile (the causal shape, 4
+// queries per wave at G = 8, measured 2-3% faster).  D = 128 keeps four waves, three workgroups to a
+// CU: six- and eight-wave workgroups (two and one to a CU) measured 33% and 21% slower there.
 template <int D, int G>
-__global__ __launch_bounds__(256, D == 128 && (G <= 4 || G == 32) ? 3 : 1) void window_fwd_mfma(WindowParams p, int tiles_per_seq, int n_tiles) {
+constexpr int waves_per_wg() {
+  return D == 64 ? 8 : 4;
+}
+
+template <int D, int G>
+__global__ __launch_bounds__((64 * waves_per_wg<D, G>()), (D == 64 ? 4 : (G <= 4 || G == 32) ? 3 : 1)) void window_fwd_mfma(WindowParams p, int tiles_per_seq, int n_tiles) {
   using Tile = SwizzledTile<D>;
   // D = 128 runs three workgroups per CU: a 3-slot ring (48 KB of LDS) and LDS addresses derived
   // by XOR from one base per operand instead of one register per read (168 VGPRs; G = 8 and 16
@@ -63,14 +73,20 @@ __global__ __launch_bounds__(256, D == 128 && (G <= 4 || G == 32) ? 3 : 1) void 
   constexpr bool kXorAddr = D == 128;
   constexpr int S = D / 16;
   constexpr int DB = D / 32;
+  constexpr int NW = waves_per_wg<D, G>();
   constexpr int QW = 32 / G;                  // queries per wave
-  constexpr int QT = 4 * QW;                  // queries per tile
-  constexpr int DPW = Tile::kDmaPerTile / 4;  // DMA instructions per wave per 32-row tile
+  constexpr int QT = NW * QW;                 // queries per tile
   constexpr int kSlot = 2 * Tile::kBytes;     // K tile + V tile
-  constexpr int kDmaPerSlot = 2 * DPW;        // DMA instructions per wave per slot
+  // The slot's 1 KB DMA instructions (K tile, then V tile) are dealt out evenly over the waves: with
+  // at most one wave per K instruction, wave w takes K instructions w h .. w h + h - 1 and the same
+  // V instructions (the same source offsets); with twice as many waves, wave w takes instruction w.
+  constexpr int kSlotDma = 2 * Tile::kDmaPerTile;
+  constexpr int kDmaPerWave = kSlotDma / NW;
+  constexpr int kSrcRegs = kDmaPerWave == 1 ? 1 : kDmaPerWave / 2;  // distinct source offsets
+  static_assert(kSlotDma % NW == 0 && (kDmaPerWave == 1 || kDmaPerWave % 2 == 0), "DMA plan");
   constexpr int kStageBytes = 32 * 128;       // O staging per wave: 32 rows x 32 dims of fp32
-  static_assert(DPW >= 1, "tile too small for four waves");
-  static_assert(4 * kStageBytes <= kRing * kSlot, "staging lives in the ring");
+  static_assert(kSlotDma >= NW, "every wave takes part in the stream");
+  static_assert(NW * kStageBytes <= kRing * kSlot, "staging lives in the ring");
   __shared__ __attribute__((aligned(1024))) char ring[kRing * kSlot];
 
   // ---- which tile: XCD x takes tiles [x * per_xcd, (x + 1) * per_xcd) in dispatch order ----
@@ -115,20 +131,24 @@ __global__ __launch_bounds__(256, D == 128 && (G <= 4 || G == 32) ? 3 : 1) void 
   const uint32_t kv_bytes = kv_span > 0x7fffffff ? 0x7fffffffu : static_cast<uint32_t>(kv_span);
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(static_cast<const __bf16 *>(p.k) + kv0, kv_bytes);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(static_cast<const __bf16 *>(p.v) + kv0, kv_bytes);
-  uint32_t kv_src[DPW];
+  auto dma_index = [&](int u) {  // wave-uniform; request 2k + t: K (t = 0) or V (t = 1) instruction w h + k
+    if constexpr (kDmaPerWave == 1) return wave;
+    else return (u & 1) * Tile::kDmaPerTile + wave * kSrcRegs + (u >> 1);
+  };
+  uint32_t kv_src[kSrcRegs];
 #pragma unroll
-  for (int u = 0; u < DPW; ++u) {
+  for (int u = 0; u < kSrcRegs; ++u) {
     int row, chunk;
-    Tile::dma_source(wave * DPW + u, lane, row, chunk);
+    Tile::dma_source(dma_index(kDmaPerWave == 1 ? u : 2 * u) % Tile::kDmaPerTile, lane, row, chunk);
     kv_src[u] = static_cast<uint32_t>(row) * kv_tok + chunk * 16;
   }
   auto issue = [&](auto I, int blk) {  // block blk (any index) into ring slot I
     constexpr int off = decltype(I)::value * kSlot;
     const uint32_t row0 = blk < nblk ? static_cast<uint32_t>(lo_wg + blk * kBlockKeys) * kv_tok : kNoData;
 #pragma unroll
-    for (int u = 0; u < DPW; ++u) {
-      dma16(krs, ring + off + (wave * DPW + u) * 1024, row0 + kv_src[u]);
-      dma16(vrs, ring + off + Tile::kBytes + (wave * DPW + u) * 1024, row0 + kv_src[u]);
+    for (int u = 0; u < kDmaPerWave; ++u) {
+      const int d = dma_index(u);
+      dma16(d < Tile::kDmaPerTile ? krs : vrs, ring + off + d * 1024, row0 + kv_src[kDmaPerWave == 1 ? 0 : u >> 1]);
     }
   };
 
@@ -263,7 +283,7 @@ __global__ __launch_bounds__(256, D == 128 && (G <= 4 || G == 32) ? 3 : 1) void 
   // fixed wait covers every step, the first included.
   auto step = [&](auto I, int j) {
     constexpr int i = decltype(I)::value;
-    wait_vmcnt<(kRing - 2) * kDmaPerSlot>();
+    wait_vmcnt<(kRing - 2) * kDmaPerWave>();
     __builtin_amdgcn_s_barrier();
     issue(Idx<(i + kRing - 1) % kRing>{}, j + kRing - 1);  // the slot block j - 1 was read from
     const int kb0 = lo_wg + j * kBlockKeys;
@@ -330,18 +350,19 @@ __global__ __launch_bounds__(256, D == 128 && (G <= 4 || G == 32) ? 3 : 1) void 
 
 template <int D, int G>
 hipError_t launch(const WindowParams &p, hipStream_t stream) {
-  constexpr int QT = 4 * (32 / G);
+  constexpr int NW = waves_per_wg<D, G>();
+  constexpr int QT = NW * (32 / G);
   const int64_t tiles_per_seq = (p.max_seqlen + QT - 1) / QT;
   const int64_t n_tiles = tiles_per_seq * p.num_seqs * p.num_kv_heads;
   if (n_tiles <= 0) return hipSuccess;
   const int64_t per_xcd = (n_tiles + kXcds - 1) / kXcds;
   if (per_xcd * kXcds > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (trace_on())
-    trace("window_fwd_mfma<D=%d, G=%d> grid=%lld block=256 tiles=%lld (%lld per sequence, %d queries each) seqs=%d "
-          "kv_heads=%d window=(%d, %d) sink_mode=%d", D, G, static_cast<long long>(per_xcd * kXcds),
+    trace("window_fwd_mfma<D=%d, G=%d> grid=%lld block=%d tiles=%lld (%lld per sequence, %d queries each) seqs=%d "
+          "kv_heads=%d window=(%d, %d) sink_mode=%d", D, G, static_cast<long long>(per_xcd * kXcds), 64 * NW,
           static_cast<long long>(n_tiles), static_cast<long long>(tiles_per_seq), QT, p.num_seqs, p.num_kv_heads,
           p.window_left, p.window_right, p.sink_mode);
-  hipLaunchKernelGGL((window_fwd_mfma<D, G>), dim3(static_cast<unsigned>(per_xcd * kXcds)), dim3(256), 0, stream, p,
+  hipLaunchKernelGGL((window_fwd_mfma<D, G>), dim3(static_cast<unsigned>(per_xcd * kXcds)), dim3(64 * NW), 0, stream, p,
                      static_cast<int>(tiles_per_seq), static_cast<int>(n_tiles));
   return hipGetLastError();
 }
