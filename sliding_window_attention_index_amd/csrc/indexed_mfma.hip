@@ -55,6 +55,12 @@ __device__ __forceinline__ int ds_read_i32(uint32_t addr) {
   asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(r) : "v"(addr));
   return r;
 }
+// The same without the wait: the caller ties the result to an lgkmcnt wait (lgkm_fence).
+__device__ __forceinline__ int ds_read_i32_nowait(uint32_t addr) {
+  int r;
+  asm volatile("ds_read_b32 %0, %1" : "=v"(r) : "v"(addr));
+  return r;
+}
 
 template <int I>
 struct Slot {
@@ -179,7 +185,10 @@ __global__ __launch_bounds__(256) void indexed_fwd_mfma(IndexedParams p) {
 
   // Block in ring slot I (attention: compile-time) or `slot` (block mass, which keeps one
   // address register and XORs at every block: there the unrolled slot loop measured slower).
-  auto compute = [&](auto I, int slot, uint32_t vmask, uint32_t zmask) {
+  // Block j from ring slot `slot`.  The attention instantiation reads tile row n's list entry with
+  // the K operand (one LDS round trip for both) and skips the block once it is known to hold no row;
+  // the block-mass instantiation gets the masks from its caller.
+  auto compute = [&](auto I, int slot, int j, uint32_t vmask, uint32_t zmask) {
     constexpr int off = decltype(I)::value * Tile::kBytes;
     u32x4 kf[S];
     if constexpr (kMass) {
@@ -187,11 +196,18 @@ __global__ __launch_bounds__(256) void indexed_fwd_mfma(IndexedParams p) {
       asm volatile("" : "+v"(kb_));
 #pragma unroll
       for (int s = 0; s < S; ++s) kf[s] = ds_read_b128<0>(kb_ ^ (32u * s));
+      lgkm_fence<0>(kf);
     } else {
 #pragma unroll
       for (int s = 0; s < S; ++s) kf[s] = ds_read_b128<off>(kaddr[s]);
+      uint32_t xr[1];
+      xr[0] = static_cast<uint32_t>(ds_read_i32_nowait(list_addr + (j * kBlockKeys + entry_of_row(n)) * 4));
+      lgkm_fence<0>(kf);
+      lgkm_fence<0>(xr);
+      vmask = static_cast<uint32_t>(__ballot(xr[0] != kBadRow));  // tile row n's entry is a row
+      if (vmask == 0u) return;
+      zmask = key0 ? static_cast<uint32_t>(__ballot(xr[0] == 0u)) : 0u;  // ... and it is row 0
     }
-    lgkm_fence<0>(kf);
     f32x16 st = f32x16{};
 #pragma unroll
     for (int s = 0; s < S; ++s)
@@ -300,10 +316,14 @@ __global__ __launch_bounds__(256) void indexed_fwd_mfma(IndexedParams p) {
       else if (younger == 2) wait_vmcnt<2 * kDpb>();
       else if (younger == 1) wait_vmcnt<kDpb>();
       else wait_vmcnt<0>();
-      const uint32_t x = static_cast<uint32_t>(ds_read_i32(list_addr + (j * kBlockKeys + entry_of_row(n)) * 4));
-      const uint32_t vmask = static_cast<uint32_t>(__ballot(x != kBadRow));  // tile row n's entry is a row
-      const uint32_t zmask = key0 ? static_cast<uint32_t>(__ballot(x == 0u)) : 0u;  // ... and it is row 0
-      if (vmask != 0u) compute(I, j & (NT - 1), vmask, zmask);
+      if constexpr (kMass) {
+        const uint32_t x = static_cast<uint32_t>(ds_read_i32(list_addr + (j * kBlockKeys + entry_of_row(n)) * 4));
+        const uint32_t vmask = static_cast<uint32_t>(__ballot(x != kBadRow));  // tile row n's entry is a row
+        const uint32_t zmask = key0 ? static_cast<uint32_t>(__ballot(x == 0u)) : 0u;  // ... and it is row 0
+        if (vmask != 0u) compute(I, j & (NT - 1), j, vmask, zmask);
+      } else {
+        compute(I, j & (NT - 1), j, 0u, 0u);
+      }
       if constexpr (kMass) {
         if (--bin_left == 0 || (j == nblk - 1 && cend == ke)) {  // the block ends with this tile
           const float tot = halves_sum(bin_sum);
