@@ -183,11 +183,11 @@ __global__ __launch_bounds__(256) void indexed_fwd_mfma(IndexedParams p) {
     vaddr[db][1] = vbase ^ (64u * db + Tile::kRow8Xor);
   }
 
-  // Block in ring slot I (attention: compile-time) or `slot` (block mass, which keeps one
-  // address register and XORs at every block: there the unrolled slot loop measured slower).
-  // Block j from ring slot `slot`.  The attention instantiation reads tile row n's list entry with
-  // the K operand (one LDS round trip for both) and skips the block once it is known to hold no row;
-  // the block-mass instantiation gets the masks from its caller.
+  // Block j from ring slot I (attention: a compile-time slot, the reads' immediate offset) or
+  // `slot` (block mass, which keeps one address register and XORs at every block: there the
+  // unrolled slot loop measured slower).  The attention instantiation reads tile row n's list entry
+  // with the K operand (one LDS round trip for both) and skips the block once it is known to hold
+  // no row; the block-mass instantiation gets the masks from its caller.
   auto compute = [&](auto I, int slot, int j, uint32_t vmask, uint32_t zmask) {
     constexpr int off = decltype(I)::value * Tile::kBytes;
     u32x4 kf[S];
