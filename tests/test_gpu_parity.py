@@ -63,6 +63,11 @@ WINDOW_CASES = [
     ("gqa8_d128", [300, 7], 16, 2, 128, (127, 0), W.SINK_KEY0, torch.bfloat16),
     ("gqa16_d64", [90, 31], 16, 1, 64, (15, 15), W.SINK_NULL, torch.bfloat16),
     ("gqa2_d64", [260, 3], 8, 4, 64, (32, 64), W.SINK_KEY0, torch.bfloat16),
+    # D = 64 runs eight-wave workgroups: 8 * 32 / G queries a tile (256 at G = 1, 128 at G = 2, 32 at
+    # G = 8); sequences one query past, one short of and several tiles long.
+    ("mha_d64_tiles", [700, 257, 255], 4, 4, 64, (100, 60), W.SINK_KEY0, torch.bfloat16),
+    ("gqa2_d64_long_causal", [600, 129], 8, 4, 64, (-1, 0), W.SINK_NULL, torch.bfloat16),
+    ("gqa8_d64_window", [520, 33, 32], 32, 4, 64, (127, 0), W.SINK_NULL, torch.bfloat16),
     ("empty_seqs", [0, 40, 0, 1, 0], 4, 2, 64, (8, 8), W.SINK_KEY0, torch.bfloat16),
     ("valu_gqa3", [60, 9], 6, 2, 64, (7, 7), W.SINK_KEY0, torch.bfloat16),
     ("valu_d96", [45], 4, 2, 96, (5, 5), W.SINK_NULL, torch.bfloat16),
