@@ -68,7 +68,7 @@ __global__ __launch_bounds__((64 * waves_per_wg<D, G>()), (D == 64 ? 4 : (G <= 4
   // D = 128 runs three workgroups per CU: a 3-slot ring (48 KB of LDS) and LDS addresses derived
   // by XOR from one base per operand instead of one register per read (168 VGPRs; G = 8 and 16
   // index their rows with a few more registers and stay at two).  D = 64 keeps four slots and
-  // precomputed addresses (four workgroups per CU either way).
+  // precomputed addresses (116 VGPRs, four waves per SIMD).
   constexpr int kRing = D == 128 ? 3 : 4;
   constexpr bool kXorAddr = D == 128;
   constexpr int S = D / 16;
