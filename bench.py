@@ -79,13 +79,21 @@ def _with_includes(names):
     return sorted(seen)
 
 
+def _code_only(text: str) -> str:
+    """The source without its comments and blank space (// and /* */ comments; the kernel sources
+    hold no string literal with either marker), so that a comment edit keeps counters valid."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return " ".join(text.split())
+
+
 def _src_hash(workload: str | None = None) -> str:
-    """Hash of the kernel sources: of every csrc/ file, or of those a workload's launches use."""
+    """Hash of the kernel sources' code: of every csrc/ file, or of those a workload's launches use."""
     names = sorted(os.listdir(_CSRC)) if workload is None else _with_includes(KERNEL_SOURCES[workload] + ["sattn_api.cpp"])
     h = hashlib.sha256()
     for name in names:
-        with open(os.path.join(_CSRC, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(_CSRC, name), encoding="utf-8") as f:
+            h.update((name + "\n" + _code_only(f.read())).encode())
     return h.hexdigest()[:16]
 
 
