@@ -545,7 +545,7 @@ def main():
                     help="only run a plain 256 MiB device-to-device copy 5 times (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the path shards "
+        print(f"bench.py: the benchmark runs on one GPU only (asked for --gpus {args.gpus}); the path shards "
               "without exchange by sequence, query or batch row, so N GPUs run N independent copies.",
               file=sys.stderr)
         sys.exit(2)
