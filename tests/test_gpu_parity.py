@@ -21,7 +21,7 @@ import oracle
 import sliding_window_attention_index_amd as sattn
 import workloads as W
 from parity import (check_indexed, check_indexed_full, check_window, check_window_full, compare, oracle_indexed,
-                    oracle_window, run_indexed, run_window, split_slices, workspace_partials)
+                    oracle_window, run_indexed, run_window, sample_rows, split_slices, workspace_partials)
 
 pytestmark = pytest.mark.gpu
 
@@ -244,6 +244,34 @@ def test_indexed_many_tasks(dev, spec, mode):
         idx[:, ::5] = sub
     case = W.make_indexed_case(f"{name}_m{mode}", B, M, H, D, N, idx, mode, seed=10, num_splits=splits)
     _log(case.name, check_indexed(case, dev))
+
+
+LONG_LISTS = [
+    # name, B, M, H, D, N, K, pad pattern, splits, sampled rows (None: all): lists longer than one
+    # staging chunk (1024 entries in the one-wave-per-task kernel, 256-entry passes in the decode-shape
+    # kernel), so that a slice is staged and streamed in several rounds.
+    ("long_h96", 1, 4, 96, 128, 3000, 2500, "some", 1, None),        # wave-per-task, 4-tile ring, 3 chunks
+    ("long_slice_h64", 1, 3, 64, 128, 3000, 2500, "some", 1, None),  # decode-shape kernel, 10 passes
+    ("long_slice_split", 1, 4, 32, 128, 3000, 2500, "oob", 2, None), # two 1250-entry slices + merge
+    ("long_many_d64", 2, 2048, 32, 64, 3000, 1100, "some", 1, 48),   # 2-tile ring, 2 chunks, sampled rows
+]
+
+
+@pytest.mark.parametrize("spec", LONG_LISTS, ids=[c[0] for c in LONG_LISTS])
+@pytest.mark.parametrize("mode", [W.SINK_NONE, W.SINK_KEY0, W.SINK_NULL])
+def test_indexed_long_lists(dev, spec, mode):
+    name, B, M, H, D, N, K, pattern, splits, n_rows = spec
+    rng = np.random.default_rng(17)
+    idx = _edge_lists(rng, B, M, N, K, pattern)
+    if mode == W.SINK_KEY0:
+        for b in range(B):
+            for t in range(0, M, 3):
+                if not (idx[b, t] == 0).any():
+                    free = np.flatnonzero(idx[b, t] < 0)
+                    idx[b, t, free[-1] if free.size else K - 1] = 0  # row 0 late in the list
+    case = W.make_indexed_case(f"{name}_m{mode}", B, M, H, D, N, idx, mode, seed=12, num_splits=splits)
+    rows = None if n_rows is None else sample_rows(B * M, n_rows, 5, must=(0, B * M - 1))
+    _log(case.name, check_indexed(case, dev, rows=rows))
 
 
 def test_indexed_padding_bit_exact(dev):
