@@ -59,6 +59,8 @@ CASES = [
     (7, 1, 1, 32, 40, 33, 64, 33, 2, 1),      # every entry -1: o = 0, lse = sink
     (8, 1, 4096, 32, 1500, 70, 0, 5, 1, 1),   # 4096 tasks: the 2-tile-ring launch, no rotary dims
     (9, 1, 2048, 64, 1500, 100, 64, 0, 2, 2), # 8192 tasks with two slices, rotary dims
+    (10, 1, 3, 96, 3000, 1500, 64, 7, 1, 1),  # one slice of three 512-entry staging chunks, three head groups
+    (11, 1, 4, 32, 3000, 1100, 0, 0, 2, 1),   # ... and of 1100 entries, no rotary dims, null sink
 ]
 
 
