@@ -31,7 +31,13 @@ namespace sattn {
 namespace {
 
 constexpr int kBlockKeys = 32;
-constexpr int kIdxCap = 512;  // list entries staged per wave at a time
+// List entries staged per wave at a time: a whole prefill list (window plus top-k, up to 1024) with
+// the 2-slot ring, so that a task streams its blocks without a restart; 512 with the 4-slot ring,
+// whose workgroups would otherwise not fit two to a CU at rd = 0 (decode slices are short anyway).
+template <int NT>
+constexpr int idx_cap() {
+  return NT == 2 ? 1024 : 512;
+}
 // Staged stand-in for an entry that is not a row: times any of the row sizes used here (4, 64, 128
 // bytes, modulo 2^32), plus an in-row offset below 128, it lands at 0xfffe0000 or above, past the
 // end of every buffer (all are < 2^31) and far from wrapping.
@@ -152,6 +158,7 @@ __global__ __launch_bounds__(256) void indexed_fp8_mfma(IndexedParams p) {
   static_assert(kSlotBytes % 256 == 0, "slot bases keep bits 4..7 clear");
   static_assert(kSlotBytes >= 32 * 128, "the epilogue stages 32 rows of 128 bytes in a slot");
   __shared__ __attribute__((aligned(1024))) char ring[4][NT * kSlotBytes];
+  constexpr int kIdxCap = idx_cap<NT>();
   __shared__ __attribute__((aligned(16))) int32_t lists[4][kIdxCap];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
